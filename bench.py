@@ -1,0 +1,286 @@
+"""Benchmark: fp16 NT GEMM (fp32 accumulation) at M = N = K = 8192 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --pmc-pass        # short run for rocprofv3 --pmc counter passes
+
+A step is one gemm_nt_f16f32 launch over the 8192^3 synthetic workload
+(A, B ~ normal(0,1) * 0.1 rounded to fp16, seed 4), inputs resident in HBM.
+W untimed steps, then exactly K timed steps between two device
+synchronisations; one JSON line on stdout.
+
+Besides the headline, the same line carries:
+  roofline      the GEMM kernel against the dense fp16 MFMA peak, its
+                duration from HIP events recorded on the launch stream, and the
+                HBM traffic measured with rocprofv3 counters when the committed
+                summary matches the current kernel source;
+  cpu_baseline  the CPU oracle (numpy float64) on a bounded row sample of the
+                same workload, timed on this host;
+  secondary     frag_copy (2^20 tiles, every num / layout / direction) in GB/s
+                against HBM bandwidth with rotating buffers, the batched
+                4096 x (128x64x64) product and the 16384x8x16384 skinny product.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp16 NT GEMM TFLOP/s (fp32 acc) at 8192^3; % of MFMA fp16 peak"
+PEAK_TFLOPS = 2516.6       # MI355X dense fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+GEMM_SOURCES = ["fp16_matrix_core_amd/csrc/gemm_nt.hip", "fp16_matrix_core_amd/csrc/layout.hpp",
+                "fp16_matrix_core_amd/csrc/kernels.hpp"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_hash):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class StreamTimer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def time(self, fn, reps):
+        t = self.torch
+        start = t.cuda.Event(enable_timing=True)
+        end = t.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for _ in range(reps):
+            fn()
+        end.record(self.stream)
+        end.synchronize()
+        return start.elapsed_time(end) / reps      # ms per call
+
+
+def cpu_baseline(A, B, target_s=10.0):
+    """The oracle (float64 numpy: ref and bound) on a row sample of the 8192^3 workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:                                   # threadpoolctl missing: report affinity
+        threads = len(os.sched_getaffinity(0))
+    N, K = B.shape
+    rows = 256
+    oracle.gemm_nt_rows(A, B, np.arange(rows))          # warm the BLAS threads
+    t0 = time.perf_counter()
+    oracle.gemm_nt_rows(A, B, np.arange(rows))
+    dt = time.perf_counter() - t0
+    rows = int(min(A.shape[0], rows * target_s / max(dt, 1e-3)))
+    rows = max(256, rows - rows % 256)
+    t0 = time.perf_counter()
+    oracle.gemm_nt_rows(A, B, np.arange(rows))
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * N * K
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192^3 product (ref and |A||B| bound, float64), {dt:.1f} s"}
+
+
+def bench_frag(torch, f, stream, reps=20, sets=3):
+    """frag_copy GB/s over 2^20 tiles (256 MiB moved per call), rotating buffer sets."""
+    from fp16_matrix_core_amd import inputs
+    n_tiles = inputs.FRAG_TILES
+    nbytes = n_tiles * 128
+    bits = torch.from_numpy(inputs.frag_bits().view(np.int16)).cuda()
+    srcs = [bits.clone() for _ in range(sets)]
+    dsts = [torch.empty_like(bits) for _ in range(sets)]
+    timer = StreamTimer(torch, stream)
+    out = {}
+    for num in (1, 2, 4):
+        for col in (0, 1):
+            for direction, dname in ((0, "load"), (1, "store"), (2, "roundtrip")):
+                i = [0]
+
+                def call():
+                    k = i[0] % sets
+                    i[0] += 1
+                    f.frag_copy_raw(srcs[k].data_ptr(), dsts[k].data_ptr(), n_tiles, num, col, direction,
+                                    stream.cuda_stream)
+                for _ in range(3):
+                    call()
+                ms = timer.time(call, reps)
+                out[f"num{num}_{'col' if col else 'row'}_{dname}"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    vals = list(out.values())
+    return {"unit": "GB/s", "bytes_per_call": 2 * nbytes, "peak": PEAK_HBM_GBS,
+            "min_frac": round(min(vals) / PEAK_HBM_GBS, 4), "max_frac": round(max(vals) / PEAK_HBM_GBS, 4),
+            "results": out}
+
+
+def bench_batched(torch, f, stream, reps=20):
+    from fp16_matrix_core_amd import inputs
+    A, B = inputs.batched_small()
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    sets = [(a, b, torch.empty((4096, 128, 64), dtype=torch.float32, device="cuda"))]
+    sets += [(a.clone(), b.clone(), torch.empty_like(sets[0][2])) for _ in range(2)]
+    i = [0]
+
+    def call():
+        x, y, o = sets[i[0] % 3]
+        i[0] += 1
+        f.gemm_nt_batched(x, y, o)
+    for _ in range(3):
+        call()
+    ms = StreamTimer(torch, stream).time(call, reps)
+    flop = 2.0 * 4096 * 128 * 64 * 64
+    nbytes = 4096 * (128 * 64 * 2 + 64 * 64 * 2 + 128 * 64 * 4)
+    return {"plan": f.plan(128, 64, 64, 4096), "us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 2),
+            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def bench_skinny(torch, f, stream, reps=20):
+    from fp16_matrix_core_amd import inputs
+    A, B = inputs.skinny()
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    o = torch.empty((16384, 8), dtype=torch.float32, device="cuda")
+    sets = [(a, b, o), (a.clone(), b.clone(), torch.empty_like(o))]
+    i = [0]
+
+    def call():
+        x, y, z = sets[i[0] % 2]
+        i[0] += 1
+        f.gemm_nt(x, y, z)
+    for _ in range(3):
+        call()
+    ms = StreamTimer(torch, stream).time(call, reps)
+    flop = 2.0 * 16384 * 8 * 16384
+    nbytes = 16384 * 16384 * 2 + 8 * 16384 * 2 + 16384 * 8 * 4
+    return {"plan": f.plan(16384, 8, 16384), "us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 2),
+            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def pmc_pass(torch, f):
+    """Three 8192^3 launches, then three copies of 1 GiB (the counter calibration kernel)."""
+    from fp16_matrix_core_amd import inputs
+    A, B = inputs.large_square()
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    out = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        f.gemm_nt(a, b, out)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc pass done: 3 x gemm_nt 8192^3, 3 x copy of 1 GiB")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the product is not sharded "
+              "across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp16_matrix_core_amd as f
+    from fp16_matrix_core_amd import inputs
+    f.lib()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a ROCm GPU")
+    if args.pmc_pass:
+        pmc_pass(torch, f)
+        return
+
+    M = N = K = 8192
+    log("generating 8192^3 inputs (seed 4)")
+    A, B = inputs.large_square()
+    a = torch.from_numpy(A).cuda()
+    b = torch.from_numpy(B).cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    plan = f.plan(M, N, K)
+
+    def step():
+        f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, K, K, N, sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = start.elapsed_time(end) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    flop = 2.0 * M * N * K
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (ms_event * 1e-3) / 1e12
+    log(f"{plan}: {ms_event * 1e3:.1f} us/launch (events), {achieved:.1f} TFLOP/s")
+
+    khash = gemm_source_hash()
+    traffic = read_traffic(khash)
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "acc_dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "gemm_nt M=N=K=8192, A (M,K) and B (N,K) fp16 row-major ~ normal(0,1)*0.1 "
+                               "(seed 4), Out fp32 (M,N)", "M": M, "N": N, "K": K, "kernel": plan},
+        "pct_of_peak": round(100 * achieved / PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": plan, "us_per_launch": round(ms_event * 1e3, 2), "source_hash": khash},
+    }
+    if not args.no_secondary:
+        log("secondary: frag_copy, batched, skinny")
+        result["secondary"] = {"frag_copy": bench_frag(torch, f, stream),
+                               "batched_4096x128x64x64": bench_batched(torch, f, stream),
+                               "skinny_16384x8x16384": bench_skinny(torch, f, stream)}
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a row sample")
+        result["cpu_baseline"] = cpu_baseline(A, B)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+"""fp16_matrix_core_amd -- Python binding of libfp16mc.so (MI355X / gfx950).
+
+The binding marshals arguments only: every step of the product and of the
+fragment copy runs in the HIP kernels of ``libfp16mc.so``.  PyTorch supplies
+device memory and the current stream; nothing here computes on the CPU, and
+every entry point raises if the library is not built.
+
+    gemm_nt(a, b, out)             Out = A @ B.T  (fp16 in, fp32 out)
+    gemm_nt_batched(a, b, out)     the same for (batch, M, K) x (batch, N, K)
+    frag_copy(src, dst, num, col_major, direction)
+    plan(M, N, K, batch=1)         name of the kernel configuration used
+
+C ABI names and status codes are those of include/fp16mc.h.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "FRAG_LOAD", "FRAG_STORE", "FRAG_ROUNDTRIP", "Fp16mcError", "lib", "lib_path",
+    "gemm_nt", "gemm_nt_batched", "frag_copy", "plan", "gemm_nt_raw", "frag_copy_raw",
+]
+
+FRAG_LOAD, FRAG_STORE, FRAG_ROUNDTRIP = 0, 1, 2
+STATUS = {0: "FP16MC_OK", -1: "FP16MC_EINVAL", -2: "FP16MC_EALIGN", -3: "FP16MC_EHIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfp16mc.so"
+_lib = None
+
+
+class Fp16mcError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib():
+    """Load libfp16mc.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; run `python -m fp16_matrix_core_amd.build` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(path)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.gemm_nt_f16f32.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        L.gemm_nt_f16f32.restype = ci
+        L.gemm_nt_f16f32_batched.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, vp]
+        L.gemm_nt_f16f32_batched.restype = ci
+        L.frag_copy.argtypes = [vp, vp, i64, ci, ci, ci, vp]
+        L.frag_copy.restype = ci
+        L.gemm_nt_f16f32_plan.argtypes = [i64, i64, i64, i64]
+        L.gemm_nt_f16f32_plan.restype = ctypes.c_char_p
+        L.fp16mc_last_error.argtypes = []
+        L.fp16mc_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise Fp16mcError(status, lib().fp16mc_last_error().decode())
+
+
+def _stream_ptr(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ld(t, rows, cols):
+    """Row stride of a 2-D view; a single row may use any stride (it is never stepped)."""
+    if t.stride(-1) != 1 and cols > 1:
+        raise ValueError("innermost dimension must be contiguous")
+    if rows > 1:
+        return t.stride(-2)
+    return max(cols, 1) + (-max(cols, 1)) % 8
+
+
+def gemm_nt_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream=0):
+    """Direct call of gemm_nt_f16f32 with integer device pointers."""
+    _check(lib().gemm_nt_f16f32(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream))
+
+
+def frag_copy_raw(src_ptr, dst_ptr, num_tiles, num, col_major, direction, stream=0):
+    _check(lib().frag_copy(src_ptr, dst_ptr, num_tiles, num, int(col_major), direction, stream))
+
+
+def gemm_nt(a, b, out=None):
+    """Out = A @ B.T on the GPU. a: (M,K) fp16, b: (N,K) fp16, out: (M,N) fp32 (allocated if None)."""
+    import torch
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form A @ B.T")
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        # rows padded to a multiple of 4 floats (16-byte aligned rows); a view is returned
+        out = torch.empty((M, N + (-N) % 4), dtype=torch.float32, device=a.device)[:, :N]
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be float32 of shape (M, N)")
+    _check(lib().gemm_nt_f16f32(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                                _ld(a, M, K), _ld(b, N, K), _ld(out, M, N), _stream_ptr(a)))
+    return out
+
+
+def gemm_nt_batched(a, b, out=None):
+    """Batched Out[p] = A[p] @ B[p].T. a: (P,M,K), b: (P,N,K) fp16, out: (P,M,N) fp32."""
+    import torch
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be float16")
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form batched A @ B.T")
+    P, M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((P, M, N + (-N) % 4), dtype=torch.float32, device=a.device)[:, :, :N]
+    if out.dtype != torch.float32 or tuple(out.shape) != (P, M, N):
+        raise ValueError("out must be float32 of shape (P, M, N)")
+    _check(lib().gemm_nt_f16f32_batched(
+        a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+        _ld(a, M, K), _ld(b, N, K), _ld(out, M, N), P,
+        a.stride(0) if P > 1 else 0, b.stride(0) if P > 1 else 0, out.stride(0) if P > 1 else 0,
+        _stream_ptr(a)))
+    return out
+
+
+def frag_copy(src, dst, num, col_major, direction):
+    """Fragment copy between two contiguous device buffers of num_tiles * 128 bytes each."""
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or nbytes % 128:
+        raise ValueError("src and dst must both hold a whole number of 128-byte tiles, same size")
+    _check(lib().frag_copy(src.data_ptr(), dst.data_ptr(), nbytes // 128, num, int(bool(col_major)),
+                           direction, _stream_ptr(src)))
+    return dst
+
+
+def plan(M, N, K, batch=1):
+    name = lib().gemm_nt_f16f32_plan(M, N, K, batch)
+    return name.decode() if name is not None else None

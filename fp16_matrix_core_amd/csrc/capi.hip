@@ -1,0 +1,114 @@
+// capi.hip -- the extern "C" boundary of libfp16mc.so (declared in fp16mc.h).
+//
+// Every argument is checked on the host before any HIP call; a failed check
+// returns a negative status and records a message for fp16mc_last_error().
+// The messages follow the matrix-load page's habit of saying why a copy does
+// not fit ("doesn't fit any num in {4,2,1}").  Launches go through
+// hipLaunchKernel, whose return code becomes FP16MC_EHIP on failure.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/fp16mc.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FP16MC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+int check_gemm(const void* A, const void* B, const float* Out, int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t sA, int64_t sB,
+               int64_t sO) {
+  if (M < 0 || N < 0 || K < 0) return fail(FP16MC_EINVAL, "negative size (M=%lld, N=%lld, K=%lld)",
+                                           (long long)M, (long long)N, (long long)K);
+  if (batch < 0) return fail(FP16MC_EINVAL, "negative batch %lld", (long long)batch);
+  if (lda < K) return fail(FP16MC_EINVAL, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+  if (ldb < K) return fail(FP16MC_EINVAL, "ldb=%lld < K=%lld", (long long)ldb, (long long)K);
+  if (ldo < N) return fail(FP16MC_EINVAL, "ldo=%lld < N=%lld", (long long)ldo, (long long)N);
+  if (sA < 0 || sB < 0 || sO < 0) return fail(FP16MC_EINVAL, "negative batch stride");
+  const bool live = M > 0 && N > 0 && batch > 0;
+  if (!live) return FP16MC_OK;
+  if (K > 0 && (A == nullptr || B == nullptr)) return fail(FP16MC_EINVAL, "A or B is NULL");
+  if (Out == nullptr) return fail(FP16MC_EINVAL, "Out is NULL");
+  if (!aligned16(A) || !aligned16(B))
+    return fail(FP16MC_EALIGN, "A and B must be 16-byte aligned (8 fp16 per access)");
+  if ((lda & 7) || (ldb & 7))
+    return fail(FP16MC_EALIGN, "lda=%lld and ldb=%lld must be multiples of 8 (16-byte rows)",
+                (long long)lda, (long long)ldb);
+  if (!aligned16(Out) || (ldo & 3))
+    return fail(FP16MC_EALIGN, "Out must be 16-byte aligned and ldo=%lld a multiple of 4", (long long)ldo);
+  if (batch > 1 && ((sA & 7) || (sB & 7) || (sO & 3)))
+    return fail(FP16MC_EALIGN, "batch strides must keep 16-byte alignment (sA, sB %% 8, sO %% 4)");
+  return FP16MC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA,
+                           int64_t strideB, int64_t strideO, void* stream) {
+  const int rc = check_gemm(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO);
+  if (rc != FP16MC_OK) return rc;
+  const fp16mc::GemmPlan plan = fp16mc::choose_gemm_plan(M, N, K, batch);
+  if (plan == fp16mc::GemmPlan::kNone) return ok();
+  const int64_t grid = fp16mc::gemm_plan_grid(plan, M, N, batch);
+  if (grid > kMaxGrid) return fail(FP16MC_EINVAL, "problem needs %lld workgroups (limit %lld)",
+                                   (long long)grid, (long long)kMaxGrid);
+  fp16mc::GemmProblem p{A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO};
+  const hipError_t e = fp16mc::launch_gemm(plan, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gemm_nt_f16f32(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldo, void* stream) {
+  return gemm_nt_f16f32_batched(A, B, Out, M, N, K, lda, ldb, ldo, 1, 0, 0, 0, stream);
+}
+
+int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_major, int direction,
+              void* stream) {
+  if (num != 1 && num != 2 && num != 4)
+    return fail(FP16MC_EINVAL, "layout doesn't fit any num in {4,2,1} (num=%d)", num);
+  if (num_tiles < 0) return fail(FP16MC_EINVAL, "negative num_tiles %lld", (long long)num_tiles);
+  if (num_tiles % num)
+    return fail(FP16MC_EINVAL, "num_tiles=%lld is not a multiple of num=%d", (long long)num_tiles, num);
+  if (col_major != 0 && col_major != 1) return fail(FP16MC_EINVAL, "col_major must be 0 or 1");
+  if (direction != FRAG_LOAD && direction != FRAG_STORE && direction != FRAG_ROUNDTRIP)
+    return fail(FP16MC_EINVAL, "direction must be FRAG_LOAD, FRAG_STORE or FRAG_ROUNDTRIP");
+  if (num_tiles == 0) return ok();
+  if (src == nullptr || dst == nullptr) return fail(FP16MC_EINVAL, "src or dst is NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(FP16MC_EALIGN, "src and dst must be 16-byte aligned");
+  const hipError_t e = fp16mc::launch_frag_copy(src, dst, num_tiles / num, num, col_major != 0, direction,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* gemm_nt_f16f32_plan(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch));
+}
+
+const char* fp16mc_last_error(void) { return g_err; }
+
+}  // extern "C"

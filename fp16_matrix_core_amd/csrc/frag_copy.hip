@@ -1,0 +1,188 @@
+// frag_copy.hip -- the 8x8 b16 matrix load/store between shared memory and
+// the per-lane register fragment ("copy -> ldstmatrix": demonstration program,
+// Algorithm steps 2-4, "How inputs change the algorithm"), on gfx950.
+//
+// CDNA4 has no single warp-collective instruction that performs this
+// shuffle, so each lane reads (or writes) exactly the LDS words its fragment
+// owns:
+//   row-major image     the two b16 of a word are adjacent and 4-byte
+//                       aligned: one ds_read_b32 / ds_write_b32 per word;
+//   column-major image  the two b16 of a word sit one column (8 elements)
+//                       apart: a ds_read_u16 pair / ds_write_b16 pair.
+// One 64-lane wavefront carries two 32-lane fragments (lanes [0,32) and
+// [32,64)), i.e. two consecutive groups.
+//
+// Each workgroup walks blocks of 16 KiB of groups: the block's image moves
+// between HBM and LDS with 16-byte accesses (one contiguous 16 KiB span),
+// and its fragments move between HBM and VGPRs with each lane's num words in
+// one access (a wavefront touches 256*num contiguous bytes).  The kernel is
+// HBM-bound: 128 bytes read and 128 bytes written per tile.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace fp16mc {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int NUM>
+struct Words;
+template <>
+struct Words<1> {
+  typedef unsigned int T;
+  static __device__ __forceinline__ unsigned int get(const T& v, int) { return v; }
+  static __device__ __forceinline__ void set(T& v, int, unsigned int w) { v = w; }
+};
+template <>
+struct Words<2> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ unsigned int get(const T& v, int t) { return v[t]; }
+  static __device__ __forceinline__ void set(T& v, int t, unsigned int w) { v[t] = w; }
+};
+template <>
+struct Words<4> {
+  typedef u32x4 T;
+  static __device__ __forceinline__ unsigned int get(const T& v, int t) { return v[t]; }
+  static __device__ __forceinline__ void set(T& v, int t, unsigned int w) { v[t] = w; }
+};
+
+constexpr int kThreads = 256;
+constexpr int kBlockBytes = 16 * 1024;
+constexpr int kBlockChunks = kBlockBytes / 16;
+constexpr int kHalfWaves = kThreads / 32;
+
+// Word t of the fragment of lane `l32` (0..31), read from a group image in LDS.
+template <int NUM, bool COL>
+__device__ __forceinline__ unsigned int lds_read_word(const unsigned short* img, int l32, int t) {
+  const int r = m8n8::row(l32);
+  const int c = 2 * m8n8::col_pair(l32);
+  if constexpr (!COL) {
+    return *reinterpret_cast<const unsigned int*>(img + m8n8::image_offset(false, NUM, r, c, t));
+  } else {
+    const unsigned int lo = img[m8n8::image_offset(true, NUM, r, c, t)];
+    const unsigned int hi = img[m8n8::image_offset(true, NUM, r, c + 1, t)];
+    return lo | (hi << 16);
+  }
+}
+
+template <int NUM, bool COL>
+__device__ __forceinline__ void lds_write_word(unsigned short* img, int l32, int t, unsigned int w) {
+  const int r = m8n8::row(l32);
+  const int c = 2 * m8n8::col_pair(l32);
+  if constexpr (!COL) {
+    *reinterpret_cast<unsigned int*>(img + m8n8::image_offset(false, NUM, r, c, t)) = w;
+  } else {
+    img[m8n8::image_offset(true, NUM, r, c, t)] = static_cast<unsigned short>(w & 0xFFFFu);
+    img[m8n8::image_offset(true, NUM, r, c + 1, t)] = static_cast<unsigned short>(w >> 16);
+  }
+}
+
+// DIR: 0 load (image -> fragment), 1 store (fragment -> image), 2 roundtrip.
+template <int NUM, bool COL, int DIR>
+__global__ void __launch_bounds__(kThreads)
+frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t groups, int64_t nblocks) {
+  constexpr int kGroupBytes = 128 * NUM;
+  constexpr int kGroupsPerBlock = kBlockBytes / kGroupBytes;
+  constexpr int kGroupHalves = 64 * NUM;
+  typedef typename Words<NUM>::T W;
+
+  __shared__ __attribute__((aligned(16))) u32x4 lds_a[kBlockChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 lds_b[DIR == 2 ? kBlockChunks : 1];
+
+  const int tid = threadIdx.x;
+  const int l32 = tid & 31;
+  const int hw = tid >> 5;  // half-wave: one 32-lane fragment at a time
+
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int64_t g0 = blk * kGroupsPerBlock;
+    const int ng = static_cast<int>((groups - g0) < kGroupsPerBlock ? (groups - g0) : kGroupsPerBlock);
+    const int nchunks = ng * (kGroupBytes / 16);
+
+    if constexpr (DIR == 0 || DIR == 2) {
+      // image: HBM -> LDS
+      const u32x4* s = static_cast<const u32x4*>(src) + g0 * (kGroupBytes / 16);
+      for (int c = tid; c < nchunks; c += kThreads) lds_a[c] = s[c];
+      __syncthreads();
+      const unsigned short* img = reinterpret_cast<const unsigned short*>(lds_a);
+      for (int lg = hw; lg < ng; lg += kHalfWaves) {
+        W v;
+#pragma unroll
+        for (int t = 0; t < NUM; ++t)
+          Words<NUM>::set(v, t, lds_read_word<NUM, COL>(img + lg * kGroupHalves, l32, t));
+        if constexpr (DIR == 0) {
+          // fragment: VGPR -> HBM, lane-major
+          W* d = static_cast<W*>(dst) + (g0 + lg) * 32 + l32;
+          *d = v;
+        } else {
+          unsigned short* out = reinterpret_cast<unsigned short*>(lds_b) + lg * kGroupHalves;
+#pragma unroll
+          for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out, l32, t, Words<NUM>::get(v, t));
+        }
+      }
+      if constexpr (DIR == 2) {
+        __syncthreads();
+        u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
+        for (int c = tid; c < nchunks; c += kThreads) d[c] = lds_b[c];
+      }
+      __syncthreads();
+    } else {
+      // fragment: HBM -> VGPR -> LDS image
+      unsigned short* img = reinterpret_cast<unsigned short*>(lds_a);
+      for (int lg = hw; lg < ng; lg += kHalfWaves) {
+        const W v = *(static_cast<const W*>(src) + (g0 + lg) * 32 + l32);
+#pragma unroll
+        for (int t = 0; t < NUM; ++t)
+          lds_write_word<NUM, COL>(img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
+      }
+      __syncthreads();
+      // image: LDS -> HBM
+      u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
+      for (int c = tid; c < nchunks; c += kThreads) d[c] = lds_a[c];
+      __syncthreads();
+    }
+  }
+}
+
+template <int NUM, bool COL, int DIR>
+hipError_t launch_one(const void* src, void* dst, int64_t groups, hipStream_t stream) {
+  constexpr int kGroupsPerBlock = kBlockBytes / (128 * NUM);
+  int64_t nblocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const int64_t grid = nblocks < 2048 ? nblocks : 2048;
+  void* args[] = {const_cast<void**>(&src), &dst, &groups, &nblocks};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&frag_copy_kernel<NUM, COL, DIR>),
+                         dim3(static_cast<unsigned>(grid)), dim3(kThreads), args, 0, stream);
+}
+
+template <int NUM, bool COL>
+hipError_t launch_dir(const void* src, void* dst, int64_t groups, int dir, hipStream_t stream) {
+  switch (dir) {
+    case 0: return launch_one<NUM, COL, 0>(src, dst, groups, stream);
+    case 1: return launch_one<NUM, COL, 1>(src, dst, groups, stream);
+    default: return launch_one<NUM, COL, 2>(src, dst, groups, stream);
+  }
+}
+
+template <int NUM>
+hipError_t launch_num(const void* src, void* dst, int64_t groups, bool col, int dir, hipStream_t stream) {
+  return col ? launch_dir<NUM, true>(src, dst, groups, dir, stream)
+             : launch_dir<NUM, false>(src, dst, groups, dir, stream);
+}
+
+}  // namespace
+
+hipError_t launch_frag_copy(const void* src, void* dst, int64_t groups, int num, bool col_major,
+                            int direction, hipStream_t stream) {
+  if (groups <= 0) return hipSuccess;
+  switch (num) {
+    case 1: return launch_num<1>(src, dst, groups, col_major, direction, stream);
+    case 2: return launch_num<2>(src, dst, groups, col_major, direction, stream);
+    default: return launch_num<4>(src, dst, groups, col_major, direction, stream);
+  }
+}
+
+}  // namespace fp16mc

@@ -1,0 +1,38 @@
+// kernels.hpp -- internal interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp16mc {
+
+// One batched NT product: problem b reads A + b*sA, B + b*sB, writes Out + b*sO.
+struct GemmProblem {
+  const void* A;
+  const void* B;
+  float* Out;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldo;
+  int64_t batch;
+  int64_t sA, sB, sO;
+};
+
+// Kernel configurations, one per shape class.
+enum class GemmPlan : int {
+  kNone = 0,      // empty problem, nothing to launch
+  kWave32 = 1,    // one wavefront per 32x32 output tile (tiny problems)
+  kWg128x64 = 2,  // 4 wavefronts per 128x64 tile (small, batched, mid-size)
+  kWg256 = 3,     // 4 wavefronts per 256x256 tile (large problems)
+};
+
+GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch);
+const char* gemm_plan_name(GemmPlan plan);
+// Number of workgroups the plan launches (host-side; used to validate the grid).
+int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch);
+hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+
+// Fragment copy; `groups` = num_tiles / num.
+hipError_t launch_frag_copy(const void* src, void* dst, int64_t groups, int num, bool col_major,
+                            int direction, hipStream_t stream);
+
+}  // namespace fp16mc

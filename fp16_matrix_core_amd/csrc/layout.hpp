@@ -1,0 +1,122 @@
+// layout.hpp -- index maps of the gfx950 data path, as constexpr functions
+// usable from host and device code.
+//
+//   lds_swizzle   16-byte chunk placement inside the 128-byte LDS rows that
+//                 hold a 64-element fp16 K slice of an operand tile.
+//   mfma32        lane maps of v_mfma_f32_32x32x16_f16.
+//   mfma16        lane maps of v_mfma_f32_16x16x32_f16.
+//   m8n8          the 8x8 b16 matrix fragment of the warp-collective matrix
+//                 load/store, mapped onto 64-lane wavefronts.
+//
+// These replace the lane tables that the pages express as TileLayouts for
+// m16n8k16 and ldmatrix; they are checked on the host (bijectivity, bank
+// spread) and on the GPU by the identity and permutation products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define FP16MC_HD __host__ __device__
+
+namespace fp16mc {
+
+// ---------------------------------------------------------------------------
+// LDS swizzle.  A row of an operand tile in LDS is 64 fp16 = 128 bytes =
+// 8 chunks of 16 bytes.  Logical chunk c of row r is stored at physical chunk
+// c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1).
+//   - any 8 consecutive rows (aligned to 8) see 8 distinct keys, so a
+//     ds_read_b128 whose 8-lane groups read one logical chunk of 8
+//     consecutive rows touches every 16-byte bank group once (32 banks);
+//   - any 16 consecutive rows (aligned to 16) give distinct
+//     (row parity, physical chunk) pairs, which is the same property for a
+//     64-bank, 256-byte-wide LDS serving 16 lanes per cycle;
+//   - a row's 8 chunks stay inside the row, so row writes of 8 lanes x 16 B
+//     are always conflict-free.
+// The XOR keeps the map a bijection inside each row.
+// ---------------------------------------------------------------------------
+namespace lds_swizzle {
+constexpr int kRowBytes = 128;
+constexpr int kChunks = 8;
+FP16MC_HD constexpr int key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+FP16MC_HD constexpr int phys_chunk(int row, int chunk) { return chunk ^ key(row); }
+FP16MC_HD constexpr int offset_bytes(int row, int chunk) {
+  return row * kRowBytes + (phys_chunk(row, chunk) << 4);
+}
+}  // namespace lds_swizzle
+
+// ---------------------------------------------------------------------------
+// v_mfma_f32_32x32x16_f16: D(32x32) += X(32x16) * Y(16x32), fp16 in, fp32 acc.
+// Operands: lane l supplies 8 fp16 of X row (l % 32), and 8 fp16 of Y column
+// (l % 32), both at k = 8*(l / 32) + e, e in [0, 8).
+// Accumulator: 16 fp32 per lane; element v of lane l is
+// D[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// ---------------------------------------------------------------------------
+namespace mfma32 {
+constexpr int kM = 32, kN = 32, kK = 16, kAcc = 16;
+FP16MC_HD constexpr int operand_row(int lane) { return lane & 31; }
+FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 5) + e; }
+FP16MC_HD constexpr int acc_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 31; }
+}  // namespace mfma32
+
+// ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x32_f16: D(16x16) += X(16x32) * Y(32x16).
+// Operands: lane l supplies X row (l % 16) / Y column (l % 16) at
+// k = 8*(l / 16) + e.  Accumulator: 4 fp32 per lane, element v of lane l is
+// D[4*(l/16) + v][l % 16].
+// ---------------------------------------------------------------------------
+namespace mfma16 {
+constexpr int kM = 16, kN = 16, kK = 32, kAcc = 4;
+FP16MC_HD constexpr int operand_row(int lane) { return lane & 15; }
+FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 4) + e; }
+FP16MC_HD constexpr int acc_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 15; }
+}  // namespace mfma16
+
+// ---------------------------------------------------------------------------
+// m8n8 fragment of the matrix load/store: over a 32-lane group, lane l holds
+// row l/4 and the column pair 2*(l%4), 2*(l%4)+1 of every tile, one 32-bit
+// word per tile (even column in the low half).  A 64-lane wavefront carries
+// two such groups: lanes [0,32) and [32,64).
+// Shared-side images (in b16 units, per group of `num` tiles):
+//   row-major     r*8*num + 8*t + c      (row stride p = 8*num)
+//   column-major  (8*t + c)*8 + r        (column stride p = 8)
+// ---------------------------------------------------------------------------
+namespace m8n8 {
+FP16MC_HD constexpr int row(int lane) { return (lane & 31) >> 2; }
+FP16MC_HD constexpr int col_pair(int lane) { return lane & 3; }
+FP16MC_HD constexpr int half_of_wave(int lane) { return lane >> 5; }
+FP16MC_HD constexpr int image_offset(bool col_major, int num, int r, int c, int t) {
+  return col_major ? (8 * t + c) * 8 + r : r * 8 * num + 8 * t + c;
+}
+}  // namespace m8n8
+
+// ---------------------------------------------------------------------------
+// Workgroup -> output tile.  Consecutive workgroup ids are dispatched
+// round-robin over the 8 XCDs, each with its own L2.  xcd_remap gives each
+// XCD a contiguous range of logical tile ids (a bijection for any count);
+// grouped_tile then orders a problem's tiles in column strips of `group_m`
+// tile rows so a contiguous id range covers a compact block of the output
+// and its A and B panels are reused from that XCD's L2.
+// ---------------------------------------------------------------------------
+namespace sched {
+constexpr int kXcds = 8;
+FP16MC_HD constexpr int64_t xcd_remap(int64_t bid, int64_t total) {
+  const int64_t q = total / kXcds, r = total % kXcds;
+  const int64_t x = bid % kXcds, j = bid / kXcds;
+  return x * q + (x < r ? x : r) + j;
+}
+struct Tile {
+  int64_t m, n;
+};
+FP16MC_HD constexpr Tile grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
+  const int64_t per_group = group_m * tiles_n;
+  const int64_t g = t / per_group;
+  const int64_t first_m = g * group_m;
+  const int64_t rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int64_t in_group = t - g * per_group;
+  return Tile{first_m + in_group % rows, in_group / rows};
+}
+}  // namespace sched
+
+}  // namespace fp16mc

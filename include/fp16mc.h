@@ -1,0 +1,136 @@
+/*
+ * fp16mc.h -- C ABI of libfp16mc.so: the fp16 NT matrix product with fp32
+ * accumulation, and the 8x8 fragment copy between shared memory and
+ * registers, on one MI355X (gfx950) GPU.
+ *
+ * Conventions for every entry point
+ *   - Pointers to data are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no reference after the call returns, and never
+ *     synchronises the host: work is enqueued on `stream`, a hipStream_t passed
+ *     as void* (NULL = the null stream).
+ *   - Arguments are validated on the host before any HIP call.  A call that
+ *     fails validation enqueues nothing and returns a negative status; the
+ *     reason is then available from fp16mc_last_error() on the same thread.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef FP16MC_H
+#define FP16MC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP16MC_OK = 0,
+  FP16MC_EINVAL = -1, /* a size, stride, count, flag or pointer is invalid   */
+  FP16MC_EALIGN = -2, /* a pointer or stride breaks the 16-byte access rule   */
+  FP16MC_EHIP = -3    /* the HIP runtime refused the launch                   */
+} fp16mc_status;
+
+/*
+ * Out = A @ B.T with fp16 inputs and fp32 accumulation and output.
+ *
+ * Defined on "Warp Matrix Instructions" (introduction; the check snippet that
+ * compares with a.float() @ b.float().T) and "Blackwell Tensor Cores" (the
+ * 128x64x64 product, K accumulated slice by slice into a fresh accumulator).
+ *
+ *   Out[i*ldo + j] = sum_{k<K} A[i*lda + k] * B[j*ldb + k],  0<=i<M, 0<=j<N
+ *
+ * A: fp16, M rows of K, row stride lda elements.   (read only)
+ * B: fp16, N rows of K, row stride ldb elements.   (read only; the product
+ *    uses B transposed, so both operands are K-contiguous)
+ * Out: fp32, M rows of N, row stride ldo elements. Write only: its prior
+ *    contents are ignored (the first K slice starts from zero), and the cells
+ *    between N and ldo of each row are never touched.
+ * Result accuracy: every element within 1e-4 * sum_k |A[i,k]*B[j,k]| of the
+ *    exact sum (fp32 accumulation in an unspecified order).
+ *
+ * Preconditions (else FP16MC_EINVAL): M, N, K >= 0; lda >= K, ldb >= K,
+ *   ldo >= N; A, B non-NULL when M*K, N*K > 0; Out non-NULL when M*N > 0.
+ * Alignment (else FP16MC_EALIGN): A and B 16-byte aligned, lda and ldb
+ *   multiples of 8 (each 8-element fp16 run is one 16-byte access, the same
+ *   rule the matrix-load page states for its tile strides); Out 16-byte
+ *   aligned and ldo a multiple of 4.
+ * M == 0 or N == 0: nothing is enqueued, FP16MC_OK.  K == 0: Out = 0.
+ * Operands may not overlap Out.
+ */
+int gemm_nt_f16f32(const void* A, const void* B, float* Out,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldo, void* stream);
+
+/*
+ * `batch` independent products in one launch: problem b uses
+ * A + b*strideA, B + b*strideB, Out + b*strideO (strides in elements) with
+ * the shapes and row strides above.  Same preconditions per problem, plus
+ * batch >= 0, strides >= 0, strideA and strideB multiples of 8, strideO a
+ * multiple of 4.  batch == 1 is exactly gemm_nt_f16f32.  The problems'
+ * output ranges must not overlap.
+ */
+int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out,
+                           int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldo,
+                           int64_t batch, int64_t strideA, int64_t strideB,
+                           int64_t strideO, void* stream);
+
+/* Directions of frag_copy. */
+enum {
+  FRAG_LOAD = 0,     /* shared image  -> fragment (the ldmatrix direction)  */
+  FRAG_STORE = 1,    /* fragment      -> shared image (the stmatrix direction) */
+  FRAG_ROUNDTRIP = 2 /* image -> fragment -> image, through registers       */
+};
+
+/*
+ * The warp-collective 8x8 b16 matrix transfer between shared memory and the
+ * per-lane register fragment, for `num` tiles at a time.
+ *
+ * Defined on "copy -> ldstmatrix": the demonstration program (register layout
+ * (8,4,num,2):(4@lane,1@lane,2,1), row-major shared layout
+ * (8,4,num,2):(8num,2,8,1)), Algorithm steps 2-4 (lane 4r+c holds row r,
+ * column pair c; row- or column-major shared side with 8-element strides;
+ * the store direction mirrors the load), and "How inputs change the
+ * algorithm" (num in {1,2,4}).  A group is `num` tiles moved by one
+ * instruction.  Registers and shared memory are not host-visible, so both
+ * sides are serialised in device memory:
+ *
+ *   image    (shared side), 64*num b16 per group, groups back to back:
+ *              row-major    element (r,c) of tile t at r*8*num + 8*t + c
+ *              column-major element (r,c) of tile t at (8*t + c)*8 + r
+ *   fragment (register side), 32*num uint32 per group, lane-major:
+ *              word (g*32 + lane)*num + t holds elements (lane/4, 2*(lane%4))
+ *              in bits 0..15 and (lane/4, 2*(lane%4)+1) in bits 16..31.
+ *
+ * Inside the kernel the image passes through LDS in the given layout and each
+ * fragment word through a VGPR of the lane that owns it; one 64-lane
+ * wavefront serves two 32-lane fragments.  Only bit patterns move: NaN
+ * payloads, infinities, subnormals and -0 are preserved exactly.
+ *
+ * src, dst: device pointers, 16-byte aligned (else FP16MC_EALIGN), each
+ *   num_tiles*128 bytes, not overlapping.  LOAD reads an image and writes a
+ *   fragment; STORE the reverse; ROUNDTRIP reads an image and writes the
+ *   image it reconstructs from the fragment (bit-identical to src).
+ * num_tiles >= 0 and a multiple of num; num in {1,2,4}; col_major in {0,1};
+ *   direction one of FRAG_*  (else FP16MC_EINVAL).  num_tiles == 0: no-op.
+ */
+int frag_copy(const void* src, void* dst, int64_t num_tiles, int num,
+              int col_major, int direction, void* stream);
+
+/*
+ * Name of the kernel configuration gemm_nt_f16f32(_batched) would launch for
+ * this shape (a static string), or NULL for an empty problem.  Pure host
+ * logic, no HIP call.
+ */
+const char* gemm_nt_f16f32_plan(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/*
+ * Message describing the last failed call on this thread ("" if none).  The
+ * pointer stays valid until the next call of this library on the thread.
+ */
+const char* fp16mc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP16MC_H */

@@ -1,0 +1,221 @@
+"""GPU parity of gemm_nt_f16f32 against the CPU oracle (through the C ABI).
+
+Bar: every element finite and |gpu - ref| <= 1e-4 * sum_k |A[i,k] B[j,k]|
+(fp64 oracle); the identity and permutation cases are exact; padding cells
+of Out (between N and ldo) and the prior contents of Out never leak.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from fp16_matrix_core_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SENTINEL = float("nan")
+
+
+@pytest.fixture(scope="module")
+def f():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import fp16_matrix_core_amd as f
+    f.lib()
+    return f
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _padded(X):
+    """Rows of X in a buffer whose row stride is a multiple of 8, NaN in the gaps (never read)."""
+    R, K = X.shape
+    ld = max(8, K + (-K) % 8)
+    buf = np.full((R, ld), np.nan, np.float16)
+    buf[:, :K] = X
+    return buf, ld
+
+
+def _run(f, A, B, ldo_pad=0):
+    """Call the C ABI with Out prefilled with NaN (prior contents must be ignored)."""
+    M, K = A.shape
+    N = B.shape[0]
+    ldo = N + ldo_pad
+    ldo += (-ldo) % 4
+    out = torch.full((M, ldo), SENTINEL, dtype=torch.float32, device="cuda")
+    a_buf, lda = _padded(A)
+    b_buf, ldb = _padded(B)
+    a, b = _dev(a_buf), _dev(b_buf)
+    f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldo,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    full = out.cpu().numpy()
+    return full[:M, :N], full[:M, N:]
+
+
+def _assert_parity(got, A, B):
+    ref, bound = oracle.gemm_nt(A, B)
+    ok, worst, n_bad = oracle.within_bound(got, ref, bound)
+    assert ok, f"{n_bad} elements outside 1e-4 * bound (worst ratio {worst:.3g})"
+    return worst
+
+
+def test_single_tile_one_wavefront(f):
+    A, B = inputs.single_tile(0)
+    assert f.plan(16, 8, 16).startswith("wave32")      # one 64-lane wavefront
+    got, _ = _run(f, A, B)
+    assert got.shape == (16, 8)
+    _assert_parity(got, A, B)
+
+
+def test_single_workgroup(f):
+    A, B, _, _, _ = inputs.single_workgroup()
+    got, _ = _run(f, A, B)
+    _assert_parity(got, A, B)
+
+
+def test_identity_b_exact(f):
+    A, _, I, _, _ = inputs.single_workgroup()
+    got, _ = _run(f, A, I)
+    assert np.array_equal(got, A.astype(np.float32))
+
+
+def test_permutation_b_exact(f):
+    A, _, _, P, perm = inputs.single_workgroup()
+    got, _ = _run(f, A, P)
+    assert np.array_equal(got, A.astype(np.float32)[:, perm])
+
+
+def test_permutation_large_tiles_exact(f):
+    """A permutation product on the 256x256 configuration: any lane-map mistake permutes the output."""
+    rng = np.random.default_rng(21)
+    M, N = 8192, 1024
+    A = inputs.uniform_f16((M, N), rng)
+    perm = rng.permutation(N)
+    P = inputs.permutation_f16(perm)
+    assert f.plan(M, N, N).startswith("wg256")
+    got, _ = _run(f, A, P)
+    assert np.array_equal(got, A.astype(np.float32)[:, perm])
+
+
+def test_one_hot_products_locate_every_cell(f):
+    """A = rows of distinct one-hot K positions, B likewise: Out[i, j] = 1 iff their K positions match."""
+    M, N, K = 96, 80, 128
+    ka = np.arange(M) % K
+    kb = (np.arange(N) * 7) % K
+    A = np.zeros((M, K), np.float16)
+    B = np.zeros((N, K), np.float16)
+    A[np.arange(M), ka] = 1
+    B[np.arange(N), kb] = 1
+    got, _ = _run(f, A, B)
+    assert np.array_equal(got, (ka[:, None] == kb[None, :]).astype(np.float32))
+
+
+RAGGED = [
+    (1, 1, 1), (1, 17, 9), (17, 1, 33), (5, 7, 3), (33, 17, 70), (31, 32, 64), (64, 64, 1000),
+    (129, 65, 64), (300, 520, 200), (257, 255, 130), (1000, 1000, 72), (513, 700, 257),
+    (4100, 2050, 100), (4096, 4096, 64), (2049, 3000, 136),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_shapes(f, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N * 13 + K)
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    got, pad = _run(f, A, B, ldo_pad=5)
+    _assert_parity(got, A, B)
+    assert np.isnan(pad).all(), "ldo padding was written"
+
+
+def test_k_zero_writes_zeros(f):
+    A = np.zeros((40, 0), np.float16)
+    B = np.zeros((24, 0), np.float16)
+    M, N = 40, 24
+    out = torch.full((M, N), SENTINEL, dtype=torch.float32, device="cuda")
+    a = torch.empty(8, dtype=torch.float16, device="cuda")
+    f.gemm_nt_raw(a.data_ptr(), a.data_ptr(), out.data_ptr(), M, N, 0, 8, 8, N,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    del A, B
+
+
+def test_strided_operands_never_read_padding(f):
+    """lda, ldb > K with NaN in the gaps: a single NaN read would poison the output."""
+    rng = np.random.default_rng(31)
+    M, N, K, lda, ldb = 300, 270, 100, 136, 112
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    a_full = np.full((M, lda), np.nan, np.float16)
+    b_full = np.full((N, ldb), np.nan, np.float16)
+    a_full[:, :K] = A
+    b_full[:, :K] = B
+    a, b = _dev(a_full), _dev(b_full)
+    ldo = N + 6
+    out = torch.full((M, ldo), SENTINEL, dtype=torch.float32, device="cuda")
+    f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldo,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    full = out.cpu().numpy()
+    _assert_parity(full[:, :N], A, B)
+    assert np.isnan(full[:, N:]).all()
+
+
+def test_torch_binding_matches_raw(f):
+    rng = np.random.default_rng(41)
+    A = inputs.uniform_f16((200, 96), rng)
+    B = inputs.uniform_f16((150, 96), rng)
+    out = f.gemm_nt(_dev(A), _dev(B))
+    torch.cuda.synchronize()
+    _assert_parity(out.cpu().numpy(), A, B)
+
+
+def test_large_square_sampled_rows(f):
+    """M = N = K = 8192, normal(0,1)*0.1 (seed 4), the launch the benchmark times; 64 sampled rows checked."""
+    A, B = inputs.large_square()
+    a, b = _dev(A), _dev(B)
+    out = torch.full((8192, 8192), SENTINEL, dtype=torch.float32, device="cuda")
+    assert f.plan(8192, 8192, 8192).startswith("wg256")
+    f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), 8192, 8192, 8192, 8192, 8192, 8192,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 255, 256, 4095, 4096, 8190, 8191],
+                                     rng.choice(8192, 52, replace=False)]))
+    got = out[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref, bound = oracle.gemm_nt_rows(A, B, rows)
+    ok, worst, n_bad = oracle.within_bound(got, ref, bound)
+    assert ok, f"{n_bad} bad, worst {worst:.3g}"
+
+
+def test_batched_small(f):
+    """4096 independent 128x64 by 64x64 problems (seed 5), one launch; every element checked."""
+    A, B = inputs.batched_small()
+    out = f.gemm_nt_batched(_dev(A), _dev(B))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref, bound = oracle.gemm_nt_batched(A, B)
+    ok, worst, n_bad = oracle.within_bound(got, ref, bound)
+    assert ok, f"{n_bad} bad, worst {worst:.3g}"
+
+
+def test_batched_equals_single_calls(f):
+    rng = np.random.default_rng(51)
+    A = inputs.uniform_f16((3, 70, 40), rng)
+    B = inputs.uniform_f16((3, 50, 40), rng)
+    out = f.gemm_nt_batched(_dev(A), _dev(B))
+    torch.cuda.synchronize()
+    for p in range(3):
+        _assert_parity(out[p].cpu().numpy(), A[p], B[p])
+
+
+def test_skinny(f):
+    """M = 16384, N = 8, K = 16384 (seed 5); every element checked."""
+    A, B = inputs.skinny()
+    got, _ = _run(f, A, B)
+    _assert_parity(got, A, B)

@@ -1,0 +1,118 @@
+"""Host-only checks: the layout module (compiled for the host), the C ABI's
+exported symbols, its argument validation and its plan selection.  No call
+here reaches the GPU: every call either fails validation or is empty, and
+both return before any HIP runtime call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp16_matrix_core_amd import build as fbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp16mc.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fbuild.LIB_PATH):
+        fbuild.build()
+    import fp16_matrix_core_amd as f
+    return f.lib()
+
+
+def test_layout_module_on_host(tmp_path):
+    exe = tmp_path / "test_layout"
+    cmd = [fbuild.HIPCC, "-x", "hip", f"--offload-arch={fbuild.ARCH}", "-O1", "-std=c++17",
+           "-I", fbuild.CSRC, os.path.join(ROOT, "tests", "host", "test_layout.cpp"), "-o", str(exe)]
+    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    out = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True)
+    assert out.returncode == 0, out.stdout
+    assert out.stdout.startswith("OK"), out.stdout
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"gemm_nt_f16f32", "gemm_nt_f16f32_batched", "frag_copy", "fp16mc_last_error",
+            "gemm_nt_f16f32_plan"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    nm = subprocess.run(["nm", "-D", "--defined-only", fbuild.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), f"{n} is not a defined text symbol"
+
+
+FAKE = 0x1000       # never dereferenced: every call below fails validation first
+MISALIGNED = 0x1002
+
+
+@pytest.mark.parametrize("args,code,needle", [
+    ((FAKE, FAKE, FAKE, -1, 8, 8, 8, 8, 8), -1, "negative size"),
+    ((FAKE, FAKE, FAKE, 8, 8, 16, 8, 16, 8), -1, "lda=8 < K=16"),
+    ((FAKE, FAKE, FAKE, 8, 8, 16, 16, 8, 8), -1, "ldb=8 < K=16"),
+    ((FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 4), -1, "ldo=4 < N=8"),
+    ((0, FAKE, FAKE, 8, 8, 16, 16, 16, 8), -1, "NULL"),
+    ((FAKE, FAKE, 0, 8, 8, 16, 16, 16, 8), -1, "Out is NULL"),
+    ((MISALIGNED, FAKE, FAKE, 8, 8, 16, 16, 16, 8), -2, "16-byte aligned"),
+    ((FAKE, FAKE, FAKE, 8, 8, 12, 12, 16, 8), -2, "multiples of 8"),
+    ((FAKE, FAKE, FAKE, 8, 6, 16, 16, 16, 6), -2, "ldo=6"),
+    ((FAKE, FAKE, MISALIGNED, 8, 8, 16, 16, 16, 8), -2, "Out must be 16-byte aligned"),
+])
+def test_gemm_validation(L, args, code, needle):
+    rc = L.gemm_nt_f16f32(*args, None)
+    assert rc == code
+    assert needle in L.fp16mc_last_error().decode()
+
+
+def test_gemm_batched_validation(L):
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, -1, 0, 0, 0, None) == -1
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 12, 128, 64, None) == -2
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, -8, 128, 64, None) == -1
+
+
+def test_empty_problems_enqueue_nothing(L):
+    # M == 0 or N == 0 or batch == 0: OK without touching pointers or the GPU
+    assert L.gemm_nt_f16f32(0, 0, 0, 0, 8, 16, 16, 16, 8, None) == 0
+    assert L.gemm_nt_f16f32(0, 0, 0, 8, 0, 16, 16, 16, 0, None) == 0
+    assert L.gemm_nt_f16f32_batched(0, 0, 0, 8, 8, 16, 16, 16, 8, 0, 0, 0, 0, None) == 0
+    assert L.frag_copy(0, 0, 0, 4, 0, 0, None) == 0
+
+
+@pytest.mark.parametrize("args,code,needle", [
+    ((FAKE, FAKE, 8, 3, 0, 0), -1, "doesn't fit any num"),
+    ((FAKE, FAKE, 6, 4, 0, 0), -1, "not a multiple of num=4"),
+    ((FAKE, FAKE, -4, 4, 0, 0), -1, "negative"),
+    ((FAKE, FAKE, 8, 2, 2, 0), -1, "col_major"),
+    ((FAKE, FAKE, 8, 2, 0, 3), -1, "direction"),
+    ((0, FAKE, 8, 2, 0, 0), -1, "NULL"),
+    ((MISALIGNED, FAKE, 8, 2, 0, 1), -2, "16-byte aligned"),
+])
+def test_frag_copy_validation(L, args, code, needle):
+    assert L.frag_copy(*args, None) == code
+    assert needle in L.fp16mc_last_error().decode()
+
+
+def test_plans(L):
+    import fp16_matrix_core_amd as f
+    assert f.plan(0, 8, 8) is None
+    assert f.plan(16, 8, 16).startswith("wave32x32")
+    assert f.plan(128, 64, 64).startswith("wg128x64")
+    assert f.plan(128, 64, 64, 4096).startswith("wg128x64")
+    assert f.plan(8192, 8192, 8192).startswith("wg256x256")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import fp16_matrix_core_amd as f
+    monkeypatch.setattr(f, "_lib", None)
+    monkeypatch.setattr(f, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="not built"):
+        f.lib()

@@ -197,3 +197,13 @@ def test_fp32_accumulation_fits_the_bound():
         acc = (acc + prods[:, :, k]).astype(np.float32)
     ok, worst, _ = oracle.within_bound(acc, ref, bound)
     assert ok and worst < 1e-5
+
+
+def test_batched_is_per_problem():
+    rng = np.random.default_rng(14)
+    A = inputs.uniform_f16((3, 5, 16), rng)
+    B = inputs.uniform_f16((3, 4, 16), rng)
+    ref, bound = oracle.gemm_nt_batched(A, B)
+    for p in range(3):
+        r, b = oracle.gemm_nt_loops(A[p], B[p])
+        assert np.allclose(ref[p], r, rtol=0, atol=1e-15) and np.allclose(bound[p], b, rtol=0, atol=1e-15)
