@@ -21,7 +21,7 @@ Every function cites the passage of the pages it follows ("Warp Matrix
 Instructions", "Blackwell Tensor Cores", "copy -> ldstmatrix").
 """
 
-from .gemm import gemm_nt, gemm_nt_loops, gemm_nt_strided, gemm_nt_rows, within_bound  # noqa: F401
+from .gemm import gemm_nt, gemm_nt_loops, gemm_nt_strided, gemm_nt_rows, gemm_nt_batched, within_bound  # noqa: F401
 from .frag import (  # noqa: F401
     register_layout, shared_layout, fit_shared_layout, image_index,
     frag_load, frag_store, frag_roundtrip,

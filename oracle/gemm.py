@@ -20,7 +20,8 @@ a correct result; the bound is order-free, so it does not favour one order.
 
 import numpy as np
 
-__all__ = ["gemm_nt", "gemm_nt_loops", "gemm_nt_strided", "gemm_nt_rows", "within_bound"]
+__all__ = ["gemm_nt", "gemm_nt_loops", "gemm_nt_strided", "gemm_nt_rows", "gemm_nt_batched",
+           "within_bound"]
 
 
 def _f64(x):
@@ -97,6 +98,21 @@ def gemm_nt_rows(A, B, rows):
     """Oracle for a subset of output rows (for sampled checks at full size)."""
     rows = np.asarray(rows, dtype=np.int64)
     return gemm_nt(np.asarray(A)[rows, :], B)
+
+
+def gemm_nt_batched(A, B):
+    """Independent products: ref[p], bound[p] = gemm_nt(A[p], B[p]) for every problem p."""
+    A = np.asarray(A)
+    B = np.asarray(B)
+    if A.ndim != 3 or B.ndim != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError(f"batched shapes {A.shape}, {B.shape}")
+    P, M, _ = A.shape
+    N = B.shape[1]
+    ref = np.empty((P, M, N))
+    bound = np.empty((P, M, N))
+    for p in range(P):
+        ref[p], bound[p] = gemm_nt(A[p], B[p])
+    return ref, bound
 
 
 def within_bound(out, ref, bound, rel=1e-4):
