@@ -33,6 +33,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -45,20 +48,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
-// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.
+// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
+// of BK = 32 held in a ring of STAGES LDS stages.
 template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
-  static constexpr int BK = 64;
+  static constexpr int BK = 32;
+  static constexpr int STAGES = 4;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int SI = WTM / 32, SJ = WTN / 32;
   static constexpr int A_STAGE = BM * lds_swizzle::kRowBytes;
   static constexpr int B_STAGE = BN * lds_swizzle::kRowBytes;
-  static constexpr int ROWS_PER_PASS = NT / 8;  // rows covered by one 16-byte load per thread
+  static constexpr int ROWS_PER_WAVE = 1024 / lds_swizzle::kRowBytes;     // one 1 KiB direct load
+  static constexpr int ROWS_PER_PASS = (NT / 64) * ROWS_PER_WAVE;
   static constexpr int A_LOADS = BM / ROWS_PER_PASS;
   static constexpr int B_LOADS = BN / ROWS_PER_PASS;
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+  static_assert(BK * 2 == lds_swizzle::kRowBytes, "an LDS row holds one K slice");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
   static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "rows must split evenly");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
@@ -68,31 +75,87 @@ using CfgWave32 = Cfg<32, 32, 1, 1, 1>;
 using CfgWg128x64 = Cfg<128, 64, 4, 1, 8>;
 using CfgWg256 = Cfg<256, 256, 2, 2, 4>;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
 // Elements [k, k+8) of a row, zero past K.  `row` points at element 0.
-__device__ __forceinline__ u32x4 load_chunk(const _Float16* row, int64_t k, int64_t K) {
-  if (k + 8 <= K) return *reinterpret_cast<const u32x4*>(row + k);
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (k < K) {
-    const unsigned short* r16 = reinterpret_cast<const unsigned short*>(row);
-    unsigned int w[4] = {0u, 0u, 0u, 0u};
-    for (int e = 0; e < 8; ++e) {
-      if (k + e < K) w[e >> 1] |= static_cast<unsigned int>(r16[k + e]) << (16 * (e & 1));
-    }
-    v = u32x4{w[0], w[1], w[2], w[3]};
+// Only the last, partial K slice of a problem takes this path.
+__device__ __forceinline__ u32x4 load_chunk_masked(const _Float16* row, int64_t k, int64_t K) {
+  const unsigned short* r16 = reinterpret_cast<const unsigned short*>(row);
+  unsigned int w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (k + e < K) w[e >> 1] |= static_cast<unsigned int>(r16[k + e]) << (16 * (e & 1));
   }
-  return v;
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at lds_span + 16 l; `lds_span` and `soff` are uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned char* lds_span, unsigned voff,
+                                      unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_span, 16, voff, soff, 0, 0);
+}
+
+// Buffer descriptor over [base, base + bytes).  Both values are workgroup-
+// uniform; passing them through readfirstlane lets the compiler keep the
+// descriptor in SGPRs instead of re-checking uniformity at every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// Scheduling hints: keep `n` instructions of one kind together at this point.
+#define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
+#define SCHED_VMEM_READ(n) __builtin_amdgcn_sched_group_barrier(0x020, (n), 0)
+#define SCHED_DS_READ(n) __builtin_amdgcn_sched_group_barrier(0x100, (n), 0)
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// How many of `total` instructions go after the n-th of k MFMAs for an even spread.
+constexpr int spread(int n, int total, int k) { return (n + 1) * total / k - n * total / k; }
+
+// s_waitcnt immediate for "vmcnt(n)" with the other counters left alone (gfx9 encoding).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <class C>
-__global__ void __launch_bounds__(C::NT)
+__global__ void __launch_bounds__(C::NT, 1)
 gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, float* __restrict__ Out,
                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
                int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m, int64_t tiles_n, int64_t total) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  // One array per (operand, stage): the compiler then knows that the
+  // asynchronous LDS writes into one stage never alias reads of another.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a1[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a2[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a3[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b2[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b3[C::B_STAGE];
+  auto stage_a = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value % C::STAGES;
+    return S == 0 ? lds_a0 : S == 1 ? lds_a1 : S == 2 ? lds_a2 : lds_a3;
+  };
+  auto stage_b = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value % C::STAGES;
+    return S == 0 ? lds_b0 : S == 1 ? lds_b1 : S == 2 ? lds_b2 : lds_b3;
+  };
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN;
   const int wn = wave % C::WN;
 
@@ -107,44 +170,61 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   B += b * sB;
   Out += b * sO;
 
-  // ---- global -> LDS assignment: thread moves chunk `ch` of rows r0 + p*ROWS_PER_PASS
-  const int ch = tid & 7;
-  const int r0 = tid >> 3;
-  const _Float16* a_src[C::A_LOADS];
-  const _Float16* b_src[C::B_LOADS];
-  int a_dst[C::A_LOADS];
-  int b_dst[C::B_LOADS];
+  // ---- global -> LDS assignment ------------------------------------------------
+  // Pass p of wavefront w fills LDS rows [p*ROWS_PER_PASS + 16w, +16): lane l
+  // lands at byte 16 l of that 1 KiB span, i.e. row +l/4, physical chunk l%4,
+  // so it fetches the logical chunk that the swizzle places there.  Rows past
+  // the matrix edge re-read its last row (their results are never stored).
+  // Addresses are byte offsets inside a buffer that starts at the tile's first
+  // row: a per-lane VGPR offset plus a uniform K offset.
+  constexpr int RW = C::ROWS_PER_WAVE;
+  const int prow = lane / lds_swizzle::kChunks;
+  const int pchunk = lane % lds_swizzle::kChunks;
+  const int64_t a_rows = (M - i0) < C::BM ? (M - i0) : C::BM;
+  const int64_t b_rows = (N - j0) < C::BN ? (N - j0) : C::BN;
+  const _Float16* a_tile = A + i0 * lda;
+  const _Float16* b_tile = B + j0 * ldb;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_tile, static_cast<unsigned>(2 * ((a_rows - 1) * lda + K)));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_tile, static_cast<unsigned>(2 * ((b_rows - 1) * ldb + K)));
+  unsigned a_off[C::A_LOADS];
+  unsigned b_off[C::B_LOADS];
 #pragma unroll
   for (int p = 0; p < C::A_LOADS; ++p) {
-    const int r = r0 + p * C::ROWS_PER_PASS;
-    const int64_t gi = (i0 + r < M) ? (i0 + r) : (M - 1);
-    a_src[p] = A + gi * lda;
-    a_dst[p] = lds_swizzle::offset_bytes(r, ch);
+    const int r = p * C::ROWS_PER_PASS + RW * wave + prow;
+    const int64_t rr = r < a_rows ? r : a_rows - 1;
+    a_off[p] = static_cast<unsigned>(2 * (rr * lda + 8 * lds_swizzle::logical_chunk(r, pchunk)));
   }
 #pragma unroll
   for (int p = 0; p < C::B_LOADS; ++p) {
-    const int r = r0 + p * C::ROWS_PER_PASS;
-    const int64_t gj = (j0 + r < N) ? (j0 + r) : (N - 1);
-    b_src[p] = B + gj * ldb;
-    b_dst[p] = lds_swizzle::offset_bytes(r, ch);
+    const int r = p * C::ROWS_PER_PASS + RW * wave + prow;
+    const int64_t rr = r < b_rows ? r : b_rows - 1;
+    b_off[p] = static_cast<unsigned>(2 * (rr * ldb + 8 * lds_swizzle::logical_chunk(r, pchunk)));
   }
-
-  u32x4 ra[C::A_LOADS];
-  u32x4 rb[C::B_LOADS];
-  auto global_load = [&](int64_t k0) {
-    const int64_t k = k0 + 8 * ch;
-#pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p) ra[p] = load_chunk(a_src[p], k, K);
-#pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) rb[p] = load_chunk(b_src[p], k, K);
+  auto span = [&](int p) { return (p * C::ROWS_PER_PASS + RW * wave) * lds_swizzle::kRowBytes; };
+  constexpr int kLoads = C::A_LOADS + C::B_LOADS;   // direct loads per slice per wavefront
+  // Load number q of a full slice (A passes first, then B passes).
+  auto dma = [&](unsigned char* as, unsigned char* bs, int q, unsigned koff) {
+    if (q < C::A_LOADS) dma16(a_rsrc, as + span(q), a_off[q], koff);
+    else dma16(b_rsrc, bs + span(q - C::A_LOADS), b_off[q - C::A_LOADS], koff);
   };
-  auto lds_store = [&](int stage) {
-    unsigned char* as = smem + stage * C::A_STAGE;
-    unsigned char* bs = smem + 2 * C::A_STAGE + stage * C::B_STAGE;
+  auto dma_all = [&](unsigned char* as, unsigned char* bs, unsigned koff) {
 #pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p) *reinterpret_cast<u32x4*>(as + a_dst[p]) = ra[p];
+    for (int q = 0; q < kLoads; ++q) dma(as, bs, q, koff);
+  };
+  // Last, partial K slice: through registers with per-element masks.
+  auto load_tail = [&](unsigned char* as, unsigned char* bs, int64_t k0) {
 #pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) *reinterpret_cast<u32x4*>(bs + b_dst[p]) = rb[p];
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const int lc = lds_swizzle::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
+      const _Float16* row = a_tile + a_off[p] / 2 - 8 * lc;
+      *reinterpret_cast<u32x4*>(as + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
+    }
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p) {
+      const int lc = lds_swizzle::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
+      const _Float16* row = b_tile + b_off[p] / 2 - 8 * lc;
+      *reinterpret_cast<u32x4*>(bs + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
+    }
   };
 
   // ---- fragment reads + MFMA ------------------------------------------------
@@ -159,42 +239,134 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   const int key = lds_swizzle::key(frow);          // equal to key(row) for every fragment row
   const int a_row0 = (wm * C::WTM + frow) * lds_swizzle::kRowBytes;
   const int b_row0 = (wn * C::WTN + frow) * lds_swizzle::kRowBytes;
+  constexpr int KK = C::BK / mfma32::kK;           // 16-wide K steps per slice (2)
+  constexpr int NMF = C::SI * C::SJ;               // MFMAs per K step
+  constexpr int kFr = C::SI + C::SJ;               // fragment reads per K step
+  static_assert(KK == 2, "the phase schedule below is written for two K steps per slice");
 
-  auto compute = [&](int stage) {
-    const unsigned char* as = smem + stage * C::A_STAGE + a_row0;
-    const unsigned char* bs = smem + 2 * C::A_STAGE + stage * C::B_STAGE + b_row0;
+  struct Frags {
+    f16x8 a[C::SI];
+    f16x8 b[C::SJ];
+  };
+  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) {
+    const int pc = ((2 * kk + khalf) ^ key) << 4;
 #pragma unroll
-    for (int kk = 0; kk < C::BK / mfma32::kK; ++kk) {
-      const int pc = ((2 * kk + khalf) ^ key) << 4;
-      f16x8 af[C::SI];
-      f16x8 bf[C::SJ];
+    for (int si = 0; si < C::SI; ++si)
+      f.a[si] = *reinterpret_cast<const f16x8*>(as + a_row0 + si * 32 * lds_swizzle::kRowBytes + pc);
 #pragma unroll
-      for (int si = 0; si < C::SI; ++si)
-        af[si] = *reinterpret_cast<const f16x8*>(as + si * 32 * lds_swizzle::kRowBytes + pc);
+    for (int sj = 0; sj < C::SJ; ++sj)
+      f.b[sj] = *reinterpret_cast<const f16x8*>(bs + b_row0 + sj * 32 * lds_swizzle::kRowBytes + pc);
+  };
+  auto mfma = [&](const Frags& f, int n) {
+    const int si = n / C::SJ, sj = n % C::SJ;
+    acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[sj], f.a[si], acc[si][sj], 0, 0, 0);
+  };
+  auto mfma_all = [&](const Frags& f) {
 #pragma unroll
-      for (int sj = 0; sj < C::SJ; ++sj)
-        bf[sj] = *reinterpret_cast<const f16x8*>(bs + sj * 32 * lds_swizzle::kRowBytes + pc);
-#pragma unroll
-      for (int si = 0; si < C::SI; ++si)
-#pragma unroll
-        for (int sj = 0; sj < C::SJ; ++sj)
-          acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[sj], af[si], acc[si][sj], 0, 0, 0);
-    }
+    for (int n = 0; n < NMF; ++n) mfma(f, n);
+  };
+  // Wait until at most `n` direct loads of this thread are in flight and its
+  // LDS reads/writes are done, then make everyone's writes visible.
+  // (A plain s_barrier: a fenced __syncthreads would also wait for the loads
+  // that are meant to stay in flight.)
+  auto publish_keep = [&](auto n) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(n)::value) & ~(15 << 8));  // lgkmcnt(0) as well
+    asm volatile("s_barrier" ::: "memory");
   };
 
-  // ---- K loop: two LDS stages, one barrier per step ---------------------------
-  const int64_t nk = (K + C::BK - 1) / C::BK;
-  if (nk > 0) {
-    global_load(0);
-    lds_store(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int stage = static_cast<int>(kt & 1);
-      const bool more = kt + 1 < nk;
-      if (more) global_load((kt + 1) * C::BK);
-      compute(stage);
-      if (more) lds_store(stage ^ 1);
-      __syncthreads();
+  // ---- K loop --------------------------------------------------------------------
+  // Full slice s (32 wide) lives in stage s % 4.  Slices s+1 and s+2 are
+  // already in flight when phase s begins; phase s issues slice s+3 into the
+  // stage of slice s-1, whose reads all completed before the barrier that
+  // opened the phase.  In phase s a wavefront
+  //   1. reads the fragments of K step (s, 0);
+  //   2. issues the MFMAs of step (s-1, 1), read before the barrier, with
+  //      half of slice s+3's loads spread between them;
+  //   3. issues the MFMAs of step (s, 0) with the fragment reads of step
+  //      (s, 1) and the other half of the loads spread between them;
+  //   4. waits until slice s+1 has landed (only slices s+2 and s+3 may still
+  //      be in flight) and its own fragment reads are done; barrier.
+  // The MFMA pipe restarts after each barrier on registers that are already
+  // loaded, and every load has about two and a half phases to land.
+  const int64_t nfull = K / C::BK;
+  Frags f0, f1;
+  auto koff_of = [&](int64_t slice) {
+    // slices past the end reload the last one into an idle stage: no branch, never read
+    return static_cast<unsigned>(2 * C::BK * (slice < nfull ? slice : nfull - 1));
+  };
+  std::integral_constant<int, 2 * kLoads> keep_two;
+  auto phase = [&](auto st, int64_t s, auto pending) {
+    constexpr int S = decltype(st)::value;
+    constexpr bool kPending = decltype(pending)::value;
+    unsigned char* as = stage_a(st);
+    unsigned char* bs = stage_b(st);
+    unsigned char* an = stage_a(std::integral_constant<int, S + 3>{});
+    unsigned char* bn = stage_b(std::integral_constant<int, S + 3>{});
+    const unsigned koff = koff_of(s + 3);
+    read_frags(as, bs, 0, f0);
+    if constexpr (kPending) mfma_all(f1);
+    dma_all(an, bn, koff);
+    read_frags(as, bs, 1, f1);
+    mfma_all(f0);
+    // Issue order for the scheduler: the next step's fragment reads and the
+    // slice loads spread evenly between the MFMAs.
+    constexpr int kHalf = (kLoads + 1) / 2;
+    SCHED_DS_READ(kFr);
+    if constexpr (kPending) {
+      static_for<NMF>([&](auto n) {
+        constexpr int v = spread(decltype(n)::value, kHalf, NMF);
+        SCHED_MFMA(1);
+        if constexpr (v > 0) SCHED_VMEM_READ(v);
+      });
+    } else {
+      SCHED_VMEM_READ(kHalf);
+    }
+    static_for<NMF>([&](auto n) {
+      constexpr int d = spread(decltype(n)::value, kFr, NMF);
+      constexpr int v = spread(decltype(n)::value, kLoads - kHalf, NMF);
+      SCHED_MFMA(1);
+      if constexpr (d > 0) SCHED_DS_READ(d);
+      if constexpr (v > 0) SCHED_VMEM_READ(v);
+    });
+    publish_keep(keep_two);
+  };
+  std::integral_constant<int, 0> st0;
+  std::integral_constant<int, 1> st1;
+  std::integral_constant<int, 2> st2;
+  std::integral_constant<int, 3> st3;
+  std::integral_constant<bool, true> with_pending;
+  std::integral_constant<bool, false> first;
+  if (nfull > 0) {
+    dma_all(lds_a0, lds_b0, koff_of(0));
+    dma_all(lds_a1, lds_b1, koff_of(1));
+    dma_all(lds_a2, lds_b2, koff_of(2));
+    publish_keep(keep_two);
+    phase(st0, 0, first);
+    int64_t s = 1;
+    for (; s + 4 <= nfull; s += 4) {
+      phase(st1, s, with_pending);
+      phase(st2, s + 1, with_pending);
+      phase(st3, s + 2, with_pending);
+      phase(st0, s + 3, with_pending);
+    }
+    if (s < nfull) phase(st1, s++, with_pending);
+    if (s < nfull) phase(st2, s++, with_pending);
+    if (s < nfull) phase(st3, s++, with_pending);
+    mfma_all(f1);  // step (nfull-1, 1)
+    // drain the idle reloads before any stage is reused or the workgroup ends
+    publish_keep(std::integral_constant<int, 0>{});
+  }
+  // The partial slice, if any, goes through registers into stage nfull % 4.
+  if (K % C::BK != 0) {
+    const int st = static_cast<int>(nfull % C::STAGES);
+    unsigned char* as = st == 0 ? lds_a0 : st == 1 ? lds_a1 : st == 2 ? lds_a2 : lds_a3;
+    unsigned char* bs = st == 0 ? lds_b0 : st == 1 ? lds_b1 : st == 2 ? lds_b2 : lds_b3;
+    load_tail(as, bs, nfull * C::BK);
+    publish_keep(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      read_frags(as, bs, kk, f0);
+      mfma_all(f0);
     }
   }
 

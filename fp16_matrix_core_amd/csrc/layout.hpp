@@ -21,24 +21,27 @@
 namespace fp16mc {
 
 // ---------------------------------------------------------------------------
-// LDS swizzle.  A row of an operand tile in LDS is 64 fp16 = 128 bytes =
-// 8 chunks of 16 bytes.  Logical chunk c of row r is stored at physical chunk
-// c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1).
-//   - any 8 consecutive rows (aligned to 8) see 8 distinct keys, so a
-//     ds_read_b128 whose 8-lane groups read one logical chunk of 8
-//     consecutive rows touches every 16-byte bank group once (32 banks);
-//   - any 16 consecutive rows (aligned to 16) give distinct
-//     (row parity, physical chunk) pairs, which is the same property for a
-//     64-bank, 256-byte-wide LDS serving 16 lanes per cycle;
-//   - a row's 8 chunks stay inside the row, so row writes of 8 lanes x 16 B
-//     are always conflict-free.
+// LDS swizzle.  A row of an operand tile in LDS holds one 32-element fp16 K
+// slice: 64 bytes = 4 chunks of 16 bytes.  Logical chunk c of row r is stored
+// at physical chunk c ^ key(r), key(r) = ((r >> 1) ^ (r >> 3)) & 3.
+//   - in any aligned block of 8 rows, the 4 even rows have distinct keys and
+//     so do the 4 odd rows: a ds_read_b128 whose 8-lane groups read one
+//     logical chunk of 8 consecutive rows touches each 16-byte bank group of
+//     a 128-byte (32-bank) LDS cycle once;
+//   - in any aligned block of 16 rows, rows equal mod 4 have distinct keys:
+//     the same property for a 256-byte (64-bank) cycle serving 16 lanes;
+//   - a row's 4 chunks stay inside the row, so the direct loads, which write
+//     16 consecutive rows per wavefront as one contiguous kilobyte, are
+//     conflict-free.
 // The XOR keeps the map a bijection inside each row.
 // ---------------------------------------------------------------------------
 namespace lds_swizzle {
-constexpr int kRowBytes = 128;
-constexpr int kChunks = 8;
-FP16MC_HD constexpr int key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+constexpr int kRowBytes = 64;
+constexpr int kChunks = 4;
+FP16MC_HD constexpr int key(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 FP16MC_HD constexpr int phys_chunk(int row, int chunk) { return chunk ^ key(row); }
+// inverse map (the XOR is its own inverse): which logical chunk sits at a physical one
+FP16MC_HD constexpr int logical_chunk(int row, int phys) { return phys ^ key(row); }
 FP16MC_HD constexpr int offset_bytes(int row, int chunk) {
   return row * kRowBytes + (phys_chunk(row, chunk) << 4);
 }

@@ -25,17 +25,19 @@ static int n_checks = 0;
 static int bank_group(int byte_off, int banks) { return (byte_off % (banks * 4)) / 16; }
 
 int main() {
-  // swizzle: a bijection of the 8 chunks inside every row
+  // swizzle: a bijection of the chunks inside every row
+  const int kc = lds_swizzle::kChunks;
   for (int r = 0; r < 256; ++r) {
     std::set<int> seen;
-    for (int c = 0; c < 8; ++c) seen.insert(lds_swizzle::phys_chunk(r, c));
-    CHECK(seen.size() == 8, "swizzle not a bijection in row %d", r);
+    for (int c = 0; c < kc; ++c) seen.insert(lds_swizzle::phys_chunk(r, c));
+    CHECK((int)seen.size() == kc, "swizzle not a bijection in row %d", r);
+    for (int c = 0; c < kc; ++c) CHECK(lds_swizzle::logical_chunk(r, lds_swizzle::phys_chunk(r, c)) == c, "inverse");
   }
   // fragment reads: lanes 0..31 read rows base..base+31 at one logical chunk.
-  // 32 banks: each 8-lane group covers the 8 bank groups once.
-  // 64 banks: each 16-lane group covers the 16 bank groups once.
+  // 32 banks: each 8-lane group covers 8 distinct 16-byte bank groups.
+  // 64 banks: each 16-lane group covers 16 distinct bank groups.
   for (int base = 0; base < 256; base += 32)
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kc; ++c) {
       for (int g = 0; g < 4; ++g) {
         std::set<int> bg;
         for (int l = 8 * g; l < 8 * g + 8; ++l) bg.insert(bank_group(lds_swizzle::offset_bytes(base + l, c), 32));
@@ -47,11 +49,12 @@ int main() {
         CHECK(bg.size() == 16, "64-bank conflict base %d chunk %d group %d", base, c, g);
       }
     }
-  // row writes: 8 lanes write the 8 chunks of one row (always distinct bank groups)
-  for (int r = 0; r < 64; ++r) {
-    std::set<int> bg;
-    for (int c = 0; c < 8; ++c) bg.insert(bank_group(lds_swizzle::offset_bytes(r, c), 32));
-    CHECK(bg.size() == 8, "row write conflict row %d", r);
+  // direct loads: one wavefront writes 1 KiB = 16 whole rows contiguously
+  for (int r0 = 0; r0 < 256; r0 += 16) {
+    std::set<int> offs;
+    for (int l = 0; l < 64; ++l) offs.insert(lds_swizzle::offset_bytes(r0 + l / kc, lds_swizzle::logical_chunk(r0 + l / kc, l % kc)));
+    CHECK(offs.size() == 64 && *offs.begin() == r0 * lds_swizzle::kRowBytes &&
+          *offs.rbegin() == r0 * lds_swizzle::kRowBytes + 63 * 16, "direct-load span not contiguous");
   }
   // MFMA accumulator maps cover the output tile exactly once
   {
