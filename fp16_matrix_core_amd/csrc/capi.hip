@@ -75,6 +75,9 @@ int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, 
   const int64_t grid = fp16mc::gemm_plan_grid(plan, M, N, batch);
   if (grid > kMaxGrid) return fail(FP16MC_EINVAL, "problem needs %lld workgroups (limit %lld)",
                                    (long long)grid, (long long)kMaxGrid);
+  if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb))
+    return fail(FP16MC_EINVAL, "a %s tile of lda=%lld / ldb=%lld rows spans 2^32 bytes or more",
+                fp16mc::gemm_plan_name(plan), (long long)lda, (long long)ldb);
   fp16mc::GemmProblem p{A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO};
   const hipError_t e = fp16mc::launch_gemm(plan, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));

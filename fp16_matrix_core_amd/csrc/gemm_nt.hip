@@ -6,24 +6,25 @@
 // staged in shared memory, moved into per-lane register fragments, multiplied
 // by wavefront-collective matrix instructions -- laid out for CDNA4:
 //
-//   global -> LDS   each thread moves 16-byte chunks (8 fp16 of one row) with
-//                   one global_load_dwordx4; 8 consecutive lanes cover one
-//                   128-byte row segment, so a wavefront reads 8 full rows.
-//   LDS layout      a BK = 64 slice of a row is 128 bytes = 8 chunks, placed
+//   global -> LDS   direct loads (buffer_load_dwordx4 ... lds): each lane
+//                   moves one 16-byte chunk (8 fp16 of one row) straight into
+//                   LDS; a wavefront fills 16 whole 64-byte rows per load.
+//   LDS layout      a BK = 32 slice of a row is 64 bytes = 4 chunks, placed
 //                   by the XOR swizzle of layout.hpp (conflict-free for the
-//                   row writes and for the fragment reads below).
+//                   direct loads and for the fragment reads below).
 //   LDS -> VGPR     one ds_read_b128 per lane per operand fragment: the 8
 //                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 takes
 //                   from each lane.  Both operands are K-contiguous (NT), so
 //                   no transpose is needed.
-//   MFMA            B's fragment is the instruction's first operand and A's
-//                   the second, so the accumulator holds Out transposed:
-//                   each lane owns 4 consecutive output columns of one row
-//                   per 4 accumulator registers, stored with one 16-byte
-//                   global store.
-//   K loop          two LDS stages; the global loads of stage k+1 are issued
-//                   before the MFMAs of stage k and land in LDS after them,
-//                   one workgroup barrier per K step.
+//   MFMA            A's fragment is the instruction's first operand, B's
+//                   the second, so in each accumulator register the 32
+//                   lanes of a half-wavefront hold 32 consecutive columns of
+//                   one output row: a dword store per register writes two
+//                   whole 128-byte row segments.
+//   K loop          a ring of LDS stages; each slice's loads are issued
+//                   STAGES-1 slices ahead, spread between MFMAs, and the
+//                   fragments of the next K step are read while the current
+//                   one multiplies; one workgroup barrier per slice.
 //   scheduler       XCD-contiguous ranges of tile ids, grouped so that the
 //                   tiles an XCD runs together share A and B panels in L2.
 //   edges           rows past M or N are clamped on load (their results are
@@ -49,12 +50,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
 // (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
-// of BK = 32 held in a ring of STAGES LDS stages.
-template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_>
+// of BK = 32 held in a ring of STAGES LDS stages; WAVES_PER_SIMD workgroups'
+// worth of wavefronts share each SIMD (the register budget follows from it).
+template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
   static constexpr int BK = 32;
-  static constexpr int STAGES = 4;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int SI = WTM / 32, SJ = WTN / 32;
@@ -68,12 +71,14 @@ struct Cfg {
   static_assert(BK * 2 == lds_swizzle::kRowBytes, "an LDS row holds one K slice");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
   static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "rows must split evenly");
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static constexpr int WGS_PER_CU = WAVES_PER_SIMD * 256 / NT > 0 ? WAVES_PER_SIMD * 256 / NT : 1;
+  static_assert(LDS_BYTES * WGS_PER_CU <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
 };
 
-using CfgWave32 = Cfg<32, 32, 1, 1, 1>;
-using CfgWg128x64 = Cfg<128, 64, 4, 1, 8>;
-using CfgWg256 = Cfg<256, 256, 2, 2, 4>;
+using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
+using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 4, 1>;
+using CfgWg256 = Cfg<256, 256, 2, 2, 4, 4, 1>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -131,26 +136,27 @@ constexpr int spread(int n, int total, int k) { return (n + 1) * total / k - n *
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <class C>
-__global__ void __launch_bounds__(C::NT, 1)
+__global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD)
 gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, float* __restrict__ Out,
                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
                int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m, int64_t tiles_n, int64_t total) {
   // One array per (operand, stage): the compiler then knows that the
   // asynchronous LDS writes into one stage never alias reads of another.
+  constexpr int kS = C::STAGES;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[C::A_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_a1[C::A_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_a2[C::A_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_a3[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a2[kS > 2 ? C::A_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a3[kS > 3 ? C::A_STAGE : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[C::B_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[C::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_b2[C::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_b3[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b2[kS > 2 ? C::B_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b3[kS > 3 ? C::B_STAGE : 16];
   auto stage_a = [&](auto st) -> unsigned char* {
-    constexpr int S = decltype(st)::value % C::STAGES;
+    constexpr int S = decltype(st)::value % kS;
     return S == 0 ? lds_a0 : S == 1 ? lds_a1 : S == 2 ? lds_a2 : lds_a3;
   };
   auto stage_b = [&](auto st) -> unsigned char* {
-    constexpr int S = decltype(st)::value % C::STAGES;
+    constexpr int S = decltype(st)::value % kS;
     return S == 0 ? lds_b0 : S == 1 ? lds_b1 : S == 2 ? lds_b2 : lds_b3;
   };
 
@@ -259,7 +265,7 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   };
   auto mfma = [&](const Frags& f, int n) {
     const int si = n / C::SJ, sj = n % C::SJ;
-    acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[sj], f.a[si], acc[si][sj], 0, 0, 0);
+    acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[si], f.b[sj], acc[si][sj], 0, 0, 0);
   };
   auto mfma_all = [&](const Frags& f) {
 #pragma unroll
@@ -275,34 +281,35 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   };
 
   // ---- K loop --------------------------------------------------------------------
-  // Full slice s (32 wide) lives in stage s % 4.  Slices s+1 and s+2 are
-  // already in flight when phase s begins; phase s issues slice s+3 into the
-  // stage of slice s-1, whose reads all completed before the barrier that
-  // opened the phase.  In phase s a wavefront
+  // Full slice s (32 wide) lives in stage s % S of an S-stage ring.  Slices
+  // s+1 .. s+S-2 are already in flight when phase s begins; phase s issues
+  // slice s+S-1 into the stage of slice s-1, whose reads all completed before
+  // the barrier that opened the phase.  In phase s a wavefront
   //   1. reads the fragments of K step (s, 0);
   //   2. issues the MFMAs of step (s-1, 1), read before the barrier, with
-  //      half of slice s+3's loads spread between them;
+  //      half of slice s+S-1's loads spread between them;
   //   3. issues the MFMAs of step (s, 0) with the fragment reads of step
   //      (s, 1) and the other half of the loads spread between them;
-  //   4. waits until slice s+1 has landed (only slices s+2 and s+3 may still
-  //      be in flight) and its own fragment reads are done; barrier.
+  //   4. waits until slice s+1 has landed (only the S-2 later slices may
+  //      still be in flight) and its own fragment reads are done; barrier.
   // The MFMA pipe restarts after each barrier on registers that are already
-  // loaded, and every load has about two and a half phases to land.
+  // loaded, and every load has about S-1.5 phases to land.
+  constexpr int kAhead = kS - 1;                   // prefetch distance in slices
   const int64_t nfull = K / C::BK;
   Frags f0, f1;
   auto koff_of = [&](int64_t slice) {
     // slices past the end reload the last one into an idle stage: no branch, never read
     return static_cast<unsigned>(2 * C::BK * (slice < nfull ? slice : nfull - 1));
   };
-  std::integral_constant<int, 2 * kLoads> keep_two;
+  std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
   auto phase = [&](auto st, int64_t s, auto pending) {
     constexpr int S = decltype(st)::value;
     constexpr bool kPending = decltype(pending)::value;
     unsigned char* as = stage_a(st);
     unsigned char* bs = stage_b(st);
-    unsigned char* an = stage_a(std::integral_constant<int, S + 3>{});
-    unsigned char* bn = stage_b(std::integral_constant<int, S + 3>{});
-    const unsigned koff = koff_of(s + 3);
+    unsigned char* an = stage_a(std::integral_constant<int, S + kAhead>{});
+    unsigned char* bn = stage_b(std::integral_constant<int, S + kAhead>{});
+    const unsigned koff = koff_of(s + kAhead);
     read_frags(as, bs, 0, f0);
     if constexpr (kPending) mfma_all(f1);
     dma_all(an, bn, koff);
@@ -328,39 +335,41 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
       if constexpr (d > 0) SCHED_DS_READ(d);
       if constexpr (v > 0) SCHED_VMEM_READ(v);
     });
-    publish_keep(keep_two);
+    publish_keep(keep_later);
   };
-  std::integral_constant<int, 0> st0;
-  std::integral_constant<int, 1> st1;
-  std::integral_constant<int, 2> st2;
-  std::integral_constant<int, 3> st3;
   std::integral_constant<bool, true> with_pending;
   std::integral_constant<bool, false> first;
   if (nfull > 0) {
-    dma_all(lds_a0, lds_b0, koff_of(0));
-    dma_all(lds_a1, lds_b1, koff_of(1));
-    dma_all(lds_a2, lds_b2, koff_of(2));
-    publish_keep(keep_two);
-    phase(st0, 0, first);
+    static_for<kAhead>([&](auto i) { dma_all(stage_a(i), stage_b(i), koff_of(decltype(i)::value)); });
+    publish_keep(keep_later);
+    phase(std::integral_constant<int, 0>{}, 0, first);
     int64_t s = 1;
-    for (; s + 4 <= nfull; s += 4) {
-      phase(st1, s, with_pending);
-      phase(st2, s + 1, with_pending);
-      phase(st3, s + 2, with_pending);
-      phase(st0, s + 3, with_pending);
+    for (; s + kS <= nfull; s += kS) {
+      static_for<kS>([&](auto i) {
+        phase(std::integral_constant<int, (decltype(i)::value + 1) % kS>{}, s + decltype(i)::value, with_pending);
+      });
     }
-    if (s < nfull) phase(st1, s++, with_pending);
-    if (s < nfull) phase(st2, s++, with_pending);
-    if (s < nfull) phase(st3, s++, with_pending);
+    static_for<kS - 1>([&](auto i) {
+      if (s < nfull) {
+        phase(std::integral_constant<int, (decltype(i)::value + 1) % kS>{}, s, with_pending);
+        ++s;
+      }
+    });
     mfma_all(f1);  // step (nfull-1, 1)
     // drain the idle reloads before any stage is reused or the workgroup ends
     publish_keep(std::integral_constant<int, 0>{});
   }
-  // The partial slice, if any, goes through registers into stage nfull % 4.
+  // The partial slice, if any, goes through registers into stage nfull % S.
   if (K % C::BK != 0) {
-    const int st = static_cast<int>(nfull % C::STAGES);
-    unsigned char* as = st == 0 ? lds_a0 : st == 1 ? lds_a1 : st == 2 ? lds_a2 : lds_a3;
-    unsigned char* bs = st == 0 ? lds_b0 : st == 1 ? lds_b1 : st == 2 ? lds_b2 : lds_b3;
+    const int st = static_cast<int>(nfull % kS);
+    unsigned char* as = lds_a0;
+    unsigned char* bs = lds_b0;
+    static_for<kS>([&](auto i) {
+      if (st == decltype(i)::value) {
+        as = stage_a(i);
+        bs = stage_b(i);
+      }
+    });
     load_tail(as, bs, nfull * C::BK);
     publish_keep(std::integral_constant<int, 0>{});
 #pragma unroll
@@ -370,28 +379,18 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
     }
   }
 
-  // ---- epilogue: accumulator (Out transposed) -> fp32 rows ---------------------
-  // Element v = 4q + e of lane l in tile (si, sj) is Out[i][j] with
-  // i = i0 + wm*WTM + 32 si + l%32 and j = j0 + wn*WTN + 32 sj + 8q + 4(l/32) + e.
+  // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
+  // i = i0 + wm*WTM + 32 si + 8(v/4) + 4(l/32) + v%4, j = j0 + wn*WTN + 32 sj + l%32:
+  // one dword store per v writes two whole 128-byte row segments.
 #pragma unroll
   for (int si = 0; si < C::SI; ++si) {
-    const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_col(lane, 0);
-    if (i >= M) continue;
-    float* orow = Out + i * ldo;
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj) {
+      const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_row(lane, 4 * q);
-        const f32x4 v = {acc[si][sj][4 * q], acc[si][sj][4 * q + 1], acc[si][sj][4 * q + 2],
-                         acc[si][sj][4 * q + 3]};
-        if (j + 4 <= N) {
-          *reinterpret_cast<f32x4*>(orow + j) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j + e < N) orow[j + e] = v[e];
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+        if (i < M && j < N) Out[i * ldo + j] = acc[si][sj][v];
       }
     }
   }
@@ -447,6 +446,21 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
     case GemmPlan::kWg128x64: return tiles_of<CfgWg128x64>(M, N, batch, &tm, &tn);
     case GemmPlan::kWg256: return tiles_of<CfgWg256>(M, N, batch, &tm, &tn);
     default: return 0;
+  }
+}
+
+template <class C>
+bool fits_offsets(int64_t K, int64_t lda, int64_t ldb) {
+  const int64_t limit = int64_t(1) << 32;
+  return 2 * ((C::BM - 1) * lda + K) < limit && 2 * ((C::BN - 1) * ldb + K) < limit;
+}
+
+bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb) {
+  switch (plan) {
+    case GemmPlan::kWave32: return fits_offsets<CfgWave32>(K, lda, ldb);
+    case GemmPlan::kWg128x64: return fits_offsets<CfgWg128x64>(K, lda, ldb);
+    case GemmPlan::kWg256: return fits_offsets<CfgWg256>(K, lda, ldb);
+    default: return true;
   }
 }
 

@@ -30,6 +30,9 @@ const char* gemm_plan_name(GemmPlan plan);
 // Number of workgroups the plan launches (host-side; used to validate the grid).
 int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch);
 hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+// True when every operand tile of the plan spans fewer than 2^32 bytes (the
+// kernels address a tile through a buffer descriptor with 32-bit offsets).
+bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb);
 
 // Fragment copy; `groups` = num_tiles / num.
 hipError_t launch_frag_copy(const void* src, void* dst, int64_t groups, int num, bool col_major,

@@ -23,22 +23,24 @@ namespace fp16mc {
 // ---------------------------------------------------------------------------
 // LDS swizzle.  A row of an operand tile in LDS holds one 32-element fp16 K
 // slice: 64 bytes = 4 chunks of 16 bytes.  Logical chunk c of row r is stored
-// at physical chunk c ^ key(r), key(r) = ((r >> 1) ^ (r >> 3)) & 3.
-//   - in any aligned block of 8 rows, the 4 even rows have distinct keys and
-//     so do the 4 odd rows: a ds_read_b128 whose 8-lane groups read one
-//     logical chunk of 8 consecutive rows touches each 16-byte bank group of
-//     a 128-byte (32-bank) LDS cycle once;
-//   - in any aligned block of 16 rows, rows equal mod 4 have distinct keys:
-//     the same property for a 256-byte (64-bank) cycle serving 16 lanes;
-//   - a row's 4 chunks stay inside the row, so the direct loads, which write
-//     16 consecutive rows per wavefront as one contiguous kilobyte, are
-//     conflict-free.
+// at physical chunk c ^ key(r), key(r) = (r >> 2) & 3.
+//
+// Bank model (measured on gfx950 with collision probes and the SQ bank-
+// conflict counter): LDS has 64 banks of 4 bytes, and a ds_read_b128 is
+// served 16 lanes at a time, the four groups being the lanes with equal
+// (bit 5, bit 4 ^ bit 2) of the lane id -- e.g. lanes {0-3, 8-11, 20-23,
+// 28-31}.  Within a group no two lanes may touch the same bank.
+//   - fragment reads (lane l reads row l%32, chunk 2kk + l/32): rows r and
+//     r + 4m of one group differ in key, so the group covers 16 distinct
+//     16-byte bank quads;
+//   - direct loads write 16 whole rows (one contiguous kilobyte) per
+//     wavefront, lane l at byte 16 l: always conflict-free.
 // The XOR keeps the map a bijection inside each row.
 // ---------------------------------------------------------------------------
 namespace lds_swizzle {
 constexpr int kRowBytes = 64;
 constexpr int kChunks = 4;
-FP16MC_HD constexpr int key(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+FP16MC_HD constexpr int key(int row) { return (row >> 2) & 3; }
 FP16MC_HD constexpr int phys_chunk(int row, int chunk) { return chunk ^ key(row); }
 // inverse map (the XOR is its own inverse): which logical chunk sits at a physical one
 FP16MC_HD constexpr int logical_chunk(int row, int phys) { return phys ^ key(row); }

@@ -53,6 +53,9 @@ typedef enum {
  *   multiples of 8 (each 8-element fp16 run is one 16-byte access, the same
  *   rule the matrix-load page states for its tile strides); Out 16-byte
  *   aligned and ldo a multiple of 4.
+ * Size limit (else FP16MC_EINVAL): the kernels address each operand tile
+ *   (up to 256 rows) with 32-bit byte offsets, so 2*(255*lda + K) and
+ *   2*(255*ldb + K) must stay below 2^32 (about lda, ldb < 8.4e6).
  * M == 0 or N == 0: nothing is enqueued, FP16MC_OK.  K == 0: Out = 0.
  * Operands may not overlap Out.
  */

@@ -73,6 +73,13 @@ def test_gemm_validation(L, args, code, needle):
     assert needle in L.fp16mc_last_error().decode()
 
 
+def test_gemm_rejects_tiles_beyond_32bit_offsets(L):
+    # 8192 x 8192 problem with a huge row stride: validated before any HIP call
+    ld = 1 << 24
+    assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, 8192, 8192, 8192, ld, ld, 8192, None) == -1
+    assert "2^32" in L.fp16mc_last_error().decode()
+
+
 def test_gemm_batched_validation(L):
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, -1, 0, 0, 0, None) == -1
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 12, 128, 64, None) == -2
