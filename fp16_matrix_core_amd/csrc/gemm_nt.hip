@@ -339,7 +339,23 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   };
   std::integral_constant<bool, true> with_pending;
   std::integral_constant<bool, false> first;
-  if (nfull > 0) {
+  if (nfull > 0 && nfull <= kAhead) {
+    // Short K: every full slice fits in the ring at once -- load them all,
+    // one barrier, multiply.
+    static_for<kAhead>([&](auto i) {
+      if (decltype(i)::value < nfull) dma_all(stage_a(i), stage_b(i), koff_of(decltype(i)::value));
+    });
+    publish_keep(std::integral_constant<int, 0>{});
+    static_for<kAhead>([&](auto i) {
+      if (decltype(i)::value < nfull) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          read_frags(stage_a(i), stage_b(i), kk, f0);
+          mfma_all(f0);
+        }
+      }
+    });
+  } else if (nfull > 0) {
     static_for<kAhead>([&](auto i) { dma_all(stage_a(i), stage_b(i), koff_of(decltype(i)::value)); });
     publish_keep(keep_later);
     phase(std::integral_constant<int, 0>{}, 0, first);
@@ -359,7 +375,8 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
     // drain the idle reloads before any stage is reused or the workgroup ends
     publish_keep(std::integral_constant<int, 0>{});
   }
-  // The partial slice, if any, goes through registers into stage nfull % S.
+  // The partial slice, if any, goes through registers into stage nfull % S
+  // (unused by the short path, idle after the pipelined one).
   if (K % C::BK != 0) {
     const int st = static_cast<int>(nfull % kS);
     unsigned char* as = lds_a0;
@@ -396,6 +413,131 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny products (N <= 16): Out (M x N) = A (M x K) @ B (N x K)^T.
+// The work is a stream over A (each element used once), so A bypasses LDS:
+// every lane loads four 16-byte chunks of one row per 128-wide K block (the
+// four lanes of a row cover its 256 bytes), and B -- padded with zero
+// columns to 16 -- is loaded in the same K order, which is all the MFMA
+// needs (any K order gives the same sum as long as both operands agree).
+// v_mfma_f32_16x16x32_f16: lane l supplies row/column l%16 and 8 fp16 of K;
+// here lane (r = l%16, q = l/16) of MFMA step j uses K elements
+// kb + 32j + 8q .. +8 of its row, so each load instruction covers 64
+// contiguous bytes of 16 rows (a quarter-line per lane scattered over 256
+// bytes measured 29% slower).  The last, partial block uses K elements
+// kb + 32q + 8j instead (any order works while A and B agree).  Eight
+// wavefronts split K; their partial 64 x 16 results are summed through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kSkRows = 64;        // output rows per workgroup (4 MFMA row tiles)
+constexpr int kSkWaves = 8;        // wavefronts splitting K
+constexpr int kSkBlock = 128;      // K per block per wavefront
+
+// Four 16-byte chunks of a row at elements k + 32 j (all inside K).  With
+// k = kb + 8q the four lanes of a row read 64 contiguous bytes per load.
+__device__ __forceinline__ void sk_load(const _Float16* row, int64_t k, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const u32x4*>(row + k + 32 * j);
+}
+// The same with zeros past K (the last, partial block only).
+__device__ __forceinline__ void sk_load_masked(const _Float16* row, int64_t k, int64_t K, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = load_chunk_masked(row, k + 8 * j, K);
+}
+
+__global__ void __launch_bounds__(kSkWaves * 64, 1)
+gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, float* __restrict__ Out,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
+                      int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m) {
+  __shared__ float red[kSkWaves][kSkRows][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x / tiles_m;
+  const int64_t i0 = (blockIdx.x - b * tiles_m) * kSkRows;
+  A += b * sA;
+  B += b * sB;
+  Out += b * sO;
+
+  const int r = mfma16::operand_row(lane);   // row in a 16-row tile / column of B
+  const int q = lane >> 4;                   // 32-element quarter of the block
+  const _Float16* arow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t i = i0 + 16 * t + r;
+    arow[t] = A + (i < M ? i : M - 1) * lda;
+  }
+  // lanes past N read row N-1 (in bounds) and zero it: no divergent branch
+  const bool has_b = r < N;
+  const _Float16* brow = B + (has_b ? r : N - 1) * ldb;
+  const unsigned bmask = has_b ? 0xFFFFFFFFu : 0u;
+
+  // Full 128-wide K blocks are split evenly over the wavefronts; the last,
+  // partial block (if any) goes to the last wavefront with masked loads.
+  const int64_t nfull = K / kSkBlock;
+  const int64_t per = (nfull + kSkWaves - 1) / kSkWaves;
+  const int64_t blk0 = wave * per < nfull ? wave * per : nfull;
+  const int64_t blk1 = (blk0 + per < nfull) ? blk0 + per : nfull;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{};
+  u32x4 va[2][4][4];
+  u32x4 vb[2][4];
+  auto load = [&](int buf, int64_t blk) {
+    const int64_t k = blk * kSkBlock + 8 * q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sk_load(arow[t], k, va[buf][t]);
+    sk_load(brow, k, vb[buf]);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 bj = __builtin_bit_cast(f16x8, vb[buf][j] & bmask);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[buf][t][j]), bj, acc[t], 0, 0, 0);
+    }
+  };
+  if (blk0 < blk1) {
+    load(0, blk0);
+    int64_t blk = blk0;
+    for (; blk + 2 < blk1; blk += 2) {  // blocks blk+1 and blk+2 exist: no branch in the body
+      load(1, blk + 1);
+      mma(0);
+      load(0, blk + 2);
+      mma(1);
+    }
+    if (blk + 1 < blk1) {
+      load(1, blk + 1);
+      mma(0);
+      mma(1);
+    } else {
+      mma(0);
+    }
+  }
+  if (K % kSkBlock != 0 && wave == kSkWaves - 1) {
+    const int64_t k = nfull * kSkBlock + 32 * q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sk_load_masked(arow[t], k, K, va[0][t]);
+    sk_load_masked(brow, k, K, vb[0]);
+    mma(0);
+  }
+
+  // partial sums -> LDS: element v of lane l in row tile t is (row 16t + 4(l/16) + v, column l%16)
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][16 * t + mfma16::acc_row(lane, v)][mfma16::acc_col(lane, v)] = acc[t][v];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kSkRows * 16; e += kSkWaves * 64) {
+    const int row = e / 16, col = e % 16;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) sum += red[w][row][col];
+    const int64_t i = i0 + row;
+    if (i < M && col < N) Out[i * ldo + col] = sum;
+  }
+}
+
 template <class C>
 int64_t tiles_of(int64_t M, int64_t N, int64_t batch, int64_t* tm, int64_t* tn) {
   *tm = (M + C::BM - 1) / C::BM;
@@ -418,11 +560,24 @@ hipError_t launch(const GemmProblem& p, hipStream_t stream) {
                          dim3(static_cast<unsigned>(total)), dim3(C::NT), args, 0, stream);
 }
 
+hipError_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
+  const _Float16* A = static_cast<const _Float16*>(p.A);
+  const _Float16* B = static_cast<const _Float16*>(p.B);
+  float* Out = p.Out;
+  int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
+  int64_t sA = p.sA, sB = p.sB, sO = p.sO;
+  int64_t tiles_m = (M + kSkRows - 1) / kSkRows;
+  void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tiles_m};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_skinny_kernel),
+                         dim3(static_cast<unsigned>(tiles_m * p.batch)), dim3(kSkWaves * 64), args, 0, stream);
+}
+
 }  // namespace
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t /*K*/, int64_t batch) {
   if (M <= 0 || N <= 0 || batch <= 0) return GemmPlan::kNone;
   if (M <= 32 && N <= 32) return GemmPlan::kWave32;
+  if (N <= 16) return GemmPlan::kSkinny;
   // 256x256 tiles only where they are mostly full and there are enough of
   // them to occupy at least half of the 256 CUs.
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256) * batch;
@@ -435,6 +590,7 @@ const char* gemm_plan_name(GemmPlan plan) {
     case GemmPlan::kWave32: return "wave32x32_mfma32x32x16";
     case GemmPlan::kWg128x64: return "wg128x64_w4_mfma32x32x16";
     case GemmPlan::kWg256: return "wg256x256_w4_mfma32x32x16";
+    case GemmPlan::kSkinny: return "skinny64xN16_w8_mfma16x16x32";
     default: return nullptr;
   }
 }
@@ -445,6 +601,7 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
     case GemmPlan::kWave32: return tiles_of<CfgWave32>(M, N, batch, &tm, &tn);
     case GemmPlan::kWg128x64: return tiles_of<CfgWg128x64>(M, N, batch, &tm, &tn);
     case GemmPlan::kWg256: return tiles_of<CfgWg256>(M, N, batch, &tm, &tn);
+    case GemmPlan::kSkinny: return (M + kSkRows - 1) / kSkRows * batch;
     default: return 0;
   }
 }
@@ -469,6 +626,7 @@ hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream) 
     case GemmPlan::kWave32: return launch<CfgWave32>(p, stream);
     case GemmPlan::kWg128x64: return launch<CfgWg128x64>(p, stream);
     case GemmPlan::kWg256: return launch<CfgWg256>(p, stream);
+    case GemmPlan::kSkinny: return launch_skinny(p, stream);
     default: return hipSuccess;
   }
 }

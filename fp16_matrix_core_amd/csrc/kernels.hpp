@@ -23,6 +23,7 @@ enum class GemmPlan : int {
   kWave32 = 1,    // one wavefront per 32x32 output tile (tiny problems)
   kWg128x64 = 2,  // 4 wavefronts per 128x64 tile (small, batched, mid-size)
   kWg256 = 3,     // 4 wavefronts per 256x256 tile (large problems)
+  kSkinny = 4,    // N <= 16: 8 wavefronts split K over 64 rows, A streamed past LDS
 };
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch);

@@ -217,5 +217,43 @@ def test_batched_equals_single_calls(f):
 def test_skinny(f):
     """M = 16384, N = 8, K = 16384 (seed 5); every element checked."""
     A, B = inputs.skinny()
-    got, _ = _run(f, A, B)
+    assert f.plan(16384, 8, 16384).startswith("skinny")
+    got, pad = _run(f, A, B, ldo_pad=3)
     _assert_parity(got, A, B)
+    assert np.isnan(pad).all()
+
+
+SKINNY = [(64, 1, 128), (65, 8, 129), (1000, 16, 1000), (33, 3, 7), (4097, 5, 2048), (200, 16, 0), (128, 12, 4100)]
+
+
+@pytest.mark.parametrize("shape", SKINNY, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_ragged(f, shape):
+    """N <= 16 shapes on the skinny kernel: ragged M, N, K (incl. K = 0 and K not a multiple of 8)."""
+    M, N, K = shape
+    assert f.plan(M, N, K).startswith("skinny") or (M <= 32 and N <= 32)
+    rng = np.random.default_rng(M + 31 * N + 7 * K)
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    if K == 0:
+        out = torch.full((M, 16), SENTINEL, dtype=torch.float32, device="cuda")
+        a = torch.empty(8, dtype=torch.float16, device="cuda")
+        f.gemm_nt_raw(a.data_ptr(), a.data_ptr(), out.data_ptr(), M, N, 0, 8, 8, 16,
+                      torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        full = out.cpu().numpy()
+        assert (full[:, :N] == 0).all() and np.isnan(full[:, N:]).all()
+        return
+    got, pad = _run(f, A, B, ldo_pad=4)
+    _assert_parity(got, A, B)
+    assert np.isnan(pad).all()
+
+
+def test_skinny_batched(f):
+    rng = np.random.default_rng(61)
+    A = inputs.uniform_f16((3, 130, 256), rng)
+    B = inputs.uniform_f16((3, 8, 256), rng)
+    out = f.gemm_nt_batched(_dev(A), _dev(B))
+    torch.cuda.synchronize()
+    ref, bound = oracle.gemm_nt_batched(A, B)
+    ok, worst, n_bad = oracle.within_bound(out.cpu().numpy(), ref, bound)
+    assert ok, f"{n_bad} bad, worst {worst:.3g}"

@@ -115,6 +115,9 @@ def test_plans(L):
     assert f.plan(128, 64, 64).startswith("wg128x64")
     assert f.plan(128, 64, 64, 4096).startswith("wg128x64")
     assert f.plan(8192, 8192, 8192).startswith("wg256x256")
+    assert f.plan(16384, 8, 16384).startswith("skinny")
+    assert f.plan(100, 16, 64).startswith("skinny")
+    assert f.plan(100, 17, 64).startswith("wg128x64")
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
