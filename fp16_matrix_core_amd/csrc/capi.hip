@@ -33,7 +33,8 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+// The tile scheduler works in 32-bit arithmetic (grid x group strip < 2^32).
+constexpr int64_t kMaxGrid = int64_t(1) << 28;
 
 int check_gemm(const void* A, const void* B, const float* Out, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t sA, int64_t sB,

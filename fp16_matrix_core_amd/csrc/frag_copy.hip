@@ -12,8 +12,8 @@
 // One 64-lane wavefront carries two 32-lane fragments (lanes [0,32) and
 // [32,64)), i.e. two consecutive groups.
 //
-// Each workgroup walks blocks of 16 KiB of groups: the block's image moves
-// between HBM and LDS with 16-byte accesses (one contiguous 16 KiB span),
+// Each workgroup walks blocks of 8 KiB of groups: the block's image moves
+// between HBM and LDS with 16-byte accesses (one contiguous 8 KiB span),
 // and its fragments move between HBM and VGPRs with each lane's num words in
 // one access (a wavefront touches 256*num contiguous bytes).  The kernel is
 // HBM-bound: 128 bytes read and 128 bytes written per tile.
@@ -52,7 +52,7 @@ struct Words<4> {
 };
 
 constexpr int kThreads = 256;
-constexpr int kBlockBytes = 16 * 1024;
+constexpr int kBlockBytes = 8 * 1024;
 constexpr int kBlockChunks = kBlockBytes / 16;
 constexpr int kHalfWaves = kThreads / 32;
 
@@ -152,7 +152,7 @@ template <int NUM, bool COL, int DIR>
 hipError_t launch_one(const void* src, void* dst, int64_t groups, hipStream_t stream) {
   constexpr int kGroupsPerBlock = kBlockBytes / (128 * NUM);
   int64_t nblocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  const int64_t grid = nblocks < 2048 ? nblocks : 2048;
+  const int64_t grid = nblocks < 4096 ? nblocks : 4096;
   void* args[] = {const_cast<void**>(&src), &dst, &groups, &nblocks};
   return hipLaunchKernel(reinterpret_cast<const void*>(&frag_copy_kernel<NUM, COL, DIR>),
                          dim3(static_cast<unsigned>(grid)), dim3(kThreads), args, 0, stream);

@@ -166,12 +166,13 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   const int wn = wave % C::WN;
 
   // ---- tile scheduler -------------------------------------------------------
-  const int64_t lin = sched::xcd_remap(blockIdx.x, total);
-  const int64_t per_problem = tiles_m * tiles_n;
-  const int64_t b = lin / per_problem;
-  const sched::Tile tile = sched::grouped_tile(lin - b * per_problem, tiles_m, tiles_n, C::GROUP_M);
-  const int64_t i0 = tile.m * C::BM;
-  const int64_t j0 = tile.n * C::BN;
+  const uint32_t lin = sched::xcd_remap(blockIdx.x, static_cast<uint32_t>(total));
+  const uint32_t per_problem = static_cast<uint32_t>(tiles_m * tiles_n);
+  const uint32_t b = lin / per_problem;
+  const sched::Tile tile = sched::grouped_tile(lin - b * per_problem, static_cast<uint32_t>(tiles_m),
+                                               static_cast<uint32_t>(tiles_n), C::GROUP_M);
+  const int64_t i0 = static_cast<int64_t>(tile.m) * C::BM;
+  const int64_t j0 = static_cast<int64_t>(tile.n) * C::BN;
   A += b * sA;
   B += b * sB;
   Out += b * sO;
@@ -451,8 +452,8 @@ gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict
   __shared__ float red[kSkWaves][kSkRows][16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t b = blockIdx.x / tiles_m;
-  const int64_t i0 = (blockIdx.x - b * tiles_m) * kSkRows;
+  const uint32_t b = blockIdx.x / static_cast<uint32_t>(tiles_m);
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x - b * static_cast<uint32_t>(tiles_m)) * kSkRows;
   A += b * sA;
   B += b * sB;
   Out += b * sO;

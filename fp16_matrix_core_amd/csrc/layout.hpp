@@ -105,21 +105,23 @@ FP16MC_HD constexpr int image_offset(bool col_major, int num, int r, int c, int 
 // and its A and B panels are reused from that XCD's L2.
 // ---------------------------------------------------------------------------
 namespace sched {
-constexpr int kXcds = 8;
-FP16MC_HD constexpr int64_t xcd_remap(int64_t bid, int64_t total) {
-  const int64_t q = total / kXcds, r = total % kXcds;
-  const int64_t x = bid % kXcds, j = bid / kXcds;
+// 32-bit arithmetic: grids are limited to fewer than 2^31 workgroups, and
+// 64-bit integer division is a long instruction sequence on the GPU.
+constexpr uint32_t kXcds = 8;
+FP16MC_HD constexpr uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+  const uint32_t q = total / kXcds, r = total % kXcds;
+  const uint32_t x = bid % kXcds, j = bid / kXcds;
   return x * q + (x < r ? x : r) + j;
 }
 struct Tile {
-  int64_t m, n;
+  uint32_t m, n;
 };
-FP16MC_HD constexpr Tile grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
-  const int64_t per_group = group_m * tiles_n;
-  const int64_t g = t / per_group;
-  const int64_t first_m = g * group_m;
-  const int64_t rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-  const int64_t in_group = t - g * per_group;
+FP16MC_HD constexpr Tile grouped_tile(uint32_t t, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m) {
+  const uint32_t per_group = group_m * tiles_n;
+  const uint32_t g = t / per_group;
+  const uint32_t first_m = g * group_m;
+  const uint32_t rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const uint32_t in_group = t - g * per_group;
   return Tile{first_m + in_group % rows, in_group / rows};
 }
 }  // namespace sched

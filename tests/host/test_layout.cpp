@@ -126,22 +126,24 @@ int main() {
     CHECK(m8n8::row(32) == 0 && m8n8::half_of_wave(32) == 1, "second half of the wavefront");
   }
   // scheduler: xcd_remap and grouped_tile are bijections
-  for (int64_t total : {1, 7, 8, 9, 63, 64, 100, 1024, 1031, 4096}) {
+  for (uint32_t total : {1u, 7u, 8u, 9u, 63u, 64u, 100u, 1024u, 1031u, 4096u}) {
     std::vector<int> hit(total, 0);
-    for (int64_t b = 0; b < total; ++b) {
-      int64_t t = sched::xcd_remap(b, total);
-      CHECK(t >= 0 && t < total, "xcd_remap out of range total %lld", (long long)total);
+    for (uint32_t b = 0; b < total; ++b) {
+      uint32_t t = sched::xcd_remap(b, total);
+      CHECK(t < total, "xcd_remap out of range total %u", total);
       hit[t]++;
     }
-    for (int64_t t = 0; t < total; ++t) CHECK(hit[t] == 1, "xcd_remap not a bijection total %lld", (long long)total);
+    for (uint32_t t = 0; t < total; ++t) CHECK(hit[t] == 1, "xcd_remap not a bijection total %u", total);
   }
+  // the largest grid the C ABI accepts stays in range
+  CHECK(sched::xcd_remap(0x7FFFFFFEu, 0x7FFFFFFFu) < 0x7FFFFFFFu, "xcd_remap at the grid limit");
   for (int tm : {1, 3, 4, 5, 32, 33})
     for (int tn : {1, 2, 7, 32})
       for (int gm : {1, 4, 8}) {
         std::set<std::pair<long long, long long>> tiles;
-        for (int64_t t = 0; t < (int64_t)tm * tn; ++t) {
+        for (uint32_t t = 0; t < (uint32_t)(tm * tn); ++t) {
           sched::Tile x = sched::grouped_tile(t, tm, tn, gm);
-          CHECK(x.m >= 0 && x.m < tm && x.n >= 0 && x.n < tn, "grouped_tile out of range");
+          CHECK(x.m < (uint32_t)tm && x.n < (uint32_t)tn, "grouped_tile out of range");
           tiles.insert({x.m, x.n});
         }
         CHECK((int64_t)tiles.size() == (int64_t)tm * tn, "grouped_tile not a bijection %d %d %d", tm, tn, gm);
@@ -149,7 +151,7 @@ int main() {
   // a contiguous run of 32 ids inside one group covers a 4 x 8 block of a 32 x 32 tile grid
   {
     std::set<long long> ms, ns;
-    for (int64_t t = 0; t < 32; ++t) {
+    for (uint32_t t = 0; t < 32; ++t) {
       sched::Tile x = sched::grouped_tile(t, 32, 32, 4);
       ms.insert(x.m);
       ns.insert(x.n);
