@@ -8,10 +8,13 @@
 //
 //   global -> LDS   direct loads (buffer_load_dwordx4 ... lds): each lane
 //                   moves one 16-byte chunk (8 fp16 of one row) straight into
-//                   LDS; a wavefront fills 16 whole 64-byte rows per load.
-//   LDS layout      a BK = 32 slice of a row is 64 bytes = 4 chunks, placed
-//                   by the XOR swizzle of layout.hpp (conflict-free for the
-//                   direct loads and for the fragment reads below).
+//                   LDS; a wavefront fills 1 KiB of whole rows per load.
+//   LDS layout      a K slice of a row is BK = 32 or 64 fp16, i.e. 64 or 128
+//                   bytes = 4 or 8 chunks, placed by the XOR swizzles of
+//                   layout.hpp (conflict-free for the direct loads and for
+//                   the fragment reads below).  With BK = 64 the 8 lanes of a
+//                   row fetch one whole 128-byte line, which halves the L2
+//                   requests of BK = 32 (two half-line requests per line).
 //   LDS -> VGPR     one ds_read_b128 per lane per operand fragment: the 8
 //                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 takes
 //                   from each lane.  Both operands are K-contiguous (NT), so
@@ -50,25 +53,27 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
 // (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
-// of BK = 32 held in a ring of STAGES LDS stages; WAVES_PER_SIMD workgroups'
-// worth of wavefronts share each SIMD (the register budget follows from it).
-template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_>
+// of BK (32 or 64) held in a ring of STAGES LDS stages; WAVES_PER_SIMD
+// workgroups' worth of wavefronts share each SIMD (the register budget
+// follows from it).
+template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_, int BK_ = 32>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
-  static constexpr int BK = 32;
+  static constexpr int BK = BK_;
+  using Swz = LdsSwizzle<2 * BK_>;
   static constexpr int STAGES = STAGES_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int SI = WTM / 32, SJ = WTN / 32;
-  static constexpr int A_STAGE = BM * lds_swizzle::kRowBytes;
-  static constexpr int B_STAGE = BN * lds_swizzle::kRowBytes;
-  static constexpr int ROWS_PER_WAVE = 1024 / lds_swizzle::kRowBytes;     // one 1 KiB direct load
+  static constexpr int A_STAGE = BM * Swz::kRowBytes;
+  static constexpr int B_STAGE = BN * Swz::kRowBytes;
+  static constexpr int ROWS_PER_WAVE = 1024 / Swz::kRowBytes;     // one 1 KiB direct load
   static constexpr int ROWS_PER_PASS = (NT / 64) * ROWS_PER_WAVE;
   static constexpr int A_LOADS = BM / ROWS_PER_PASS;
   static constexpr int B_LOADS = BN / ROWS_PER_PASS;
   static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
-  static_assert(BK * 2 == lds_swizzle::kRowBytes, "an LDS row holds one K slice");
+  static_assert(BK == 32 || BK == 64, "an LDS row holds one 32- or 64-wide K slice");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
   static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "rows must split evenly");
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
@@ -77,8 +82,12 @@ struct Cfg {
 };
 
 using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
-using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 4, 1>;
-using CfgWg256 = Cfg<256, 256, 2, 2, 4, 4, 1>;
+// 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
+// by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
+using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
+// 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
+// 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
+using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -185,8 +194,8 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   // Addresses are byte offsets inside a buffer that starts at the tile's first
   // row: a per-lane VGPR offset plus a uniform K offset.
   constexpr int RW = C::ROWS_PER_WAVE;
-  const int prow = lane / lds_swizzle::kChunks;
-  const int pchunk = lane % lds_swizzle::kChunks;
+  const int prow = lane / C::Swz::kChunks;
+  const int pchunk = lane % C::Swz::kChunks;
   const int64_t a_rows = (M - i0) < C::BM ? (M - i0) : C::BM;
   const int64_t b_rows = (N - j0) < C::BN ? (N - j0) : C::BN;
   const _Float16* a_tile = A + i0 * lda;
@@ -199,15 +208,15 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   for (int p = 0; p < C::A_LOADS; ++p) {
     const int r = p * C::ROWS_PER_PASS + RW * wave + prow;
     const int64_t rr = r < a_rows ? r : a_rows - 1;
-    a_off[p] = static_cast<unsigned>(2 * (rr * lda + 8 * lds_swizzle::logical_chunk(r, pchunk)));
+    a_off[p] = static_cast<unsigned>(2 * (rr * lda + 8 * C::Swz::logical_chunk(r, pchunk)));
   }
 #pragma unroll
   for (int p = 0; p < C::B_LOADS; ++p) {
     const int r = p * C::ROWS_PER_PASS + RW * wave + prow;
     const int64_t rr = r < b_rows ? r : b_rows - 1;
-    b_off[p] = static_cast<unsigned>(2 * (rr * ldb + 8 * lds_swizzle::logical_chunk(r, pchunk)));
+    b_off[p] = static_cast<unsigned>(2 * (rr * ldb + 8 * C::Swz::logical_chunk(r, pchunk)));
   }
-  auto span = [&](int p) { return (p * C::ROWS_PER_PASS + RW * wave) * lds_swizzle::kRowBytes; };
+  auto span = [&](int p) { return (p * C::ROWS_PER_PASS + RW * wave) * C::Swz::kRowBytes; };
   constexpr int kLoads = C::A_LOADS + C::B_LOADS;   // direct loads per slice per wavefront
   // Load number q of a full slice (A passes first, then B passes).
   auto dma = [&](unsigned char* as, unsigned char* bs, int q, unsigned koff) {
@@ -222,13 +231,13 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   auto load_tail = [&](unsigned char* as, unsigned char* bs, int64_t k0) {
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
-      const int lc = lds_swizzle::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
+      const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
       const _Float16* row = a_tile + a_off[p] / 2 - 8 * lc;
       *reinterpret_cast<u32x4*>(as + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
     }
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
-      const int lc = lds_swizzle::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
+      const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
       const _Float16* row = b_tile + b_off[p] / 2 - 8 * lc;
       *reinterpret_cast<u32x4*>(bs + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
     }
@@ -243,13 +252,13 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
 
   const int frow = mfma32::operand_row(lane);      // row inside a 32-row MFMA tile
   const int khalf = lane >> 5;                     // which 8-wide K group of a 16-K step
-  const int key = lds_swizzle::key(frow);          // equal to key(row) for every fragment row
-  const int a_row0 = (wm * C::WTM + frow) * lds_swizzle::kRowBytes;
-  const int b_row0 = (wn * C::WTN + frow) * lds_swizzle::kRowBytes;
-  constexpr int KK = C::BK / mfma32::kK;           // 16-wide K steps per slice (2)
+  const int key = C::Swz::key(frow);          // equal to key(row) for every fragment row
+  const int a_row0 = (wm * C::WTM + frow) * C::Swz::kRowBytes;
+  const int b_row0 = (wn * C::WTN + frow) * C::Swz::kRowBytes;
+  constexpr int KK = C::BK / mfma32::kK;           // 16-wide K steps per slice (2 or 4)
   constexpr int NMF = C::SI * C::SJ;               // MFMAs per K step
   constexpr int kFr = C::SI + C::SJ;               // fragment reads per K step
-  static_assert(KK == 2, "the phase schedule below is written for two K steps per slice");
+  static_assert(KK % 2 == 0, "fragments alternate between two register sets");
 
   struct Frags {
     f16x8 a[C::SI];
@@ -259,10 +268,10 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
     const int pc = ((2 * kk + khalf) ^ key) << 4;
 #pragma unroll
     for (int si = 0; si < C::SI; ++si)
-      f.a[si] = *reinterpret_cast<const f16x8*>(as + a_row0 + si * 32 * lds_swizzle::kRowBytes + pc);
+      f.a[si] = *reinterpret_cast<const f16x8*>(as + a_row0 + si * 32 * C::Swz::kRowBytes + pc);
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj)
-      f.b[sj] = *reinterpret_cast<const f16x8*>(bs + b_row0 + sj * 32 * lds_swizzle::kRowBytes + pc);
+      f.b[sj] = *reinterpret_cast<const f16x8*>(bs + b_row0 + sj * 32 * C::Swz::kRowBytes + pc);
   };
   auto mfma = [&](const Frags& f, int n) {
     const int si = n / C::SJ, sj = n % C::SJ;
@@ -282,19 +291,19 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   };
 
   // ---- K loop --------------------------------------------------------------------
-  // Full slice s (32 wide) lives in stage s % S of an S-stage ring.  Slices
-  // s+1 .. s+S-2 are already in flight when phase s begins; phase s issues
-  // slice s+S-1 into the stage of slice s-1, whose reads all completed before
-  // the barrier that opened the phase.  In phase s a wavefront
+  // Full slice s lives in stage s % S of an S-stage ring.  Slices s+1 ..
+  // s+S-2 are already in flight when phase s begins; phase s issues slice
+  // s+S-1 into the stage of slice s-1, whose reads all completed before the
+  // barrier that opened the phase.  In phase s a wavefront
   //   1. reads the fragments of K step (s, 0);
-  //   2. issues the MFMAs of step (s-1, 1), read before the barrier, with
-  //      half of slice s+S-1's loads spread between them;
-  //   3. issues the MFMAs of step (s, 0) with the fragment reads of step
-  //      (s, 1) and the other half of the loads spread between them;
+  //   2. issues the MFMAs of step (s-1, KK-1), read before the barrier;
+  //   3. for kk = 1 .. KK-1 issues the MFMAs of step (s, kk-1) with the
+  //      fragment reads of step (s, kk) spread between them;
   //   4. waits until slice s+1 has landed (only the S-2 later slices may
   //      still be in flight) and its own fragment reads are done; barrier.
-  // The MFMA pipe restarts after each barrier on registers that are already
-  // loaded, and every load has about S-1.5 phases to land.
+  // Slice s+S-1's loads are spread over the MFMAs of the first two steps of
+  // 2 and 3, so that they leave early in the phase.  The MFMA pipe restarts
+  // after each barrier on registers that are already loaded.
   constexpr int kAhead = kS - 1;                   // prefetch distance in slices
   const int64_t nfull = K / C::BK;
   Frags f0, f1;
@@ -303,6 +312,7 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
     return static_cast<unsigned>(2 * C::BK * (slice < nfull ? slice : nfull - 1));
   };
   std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
+  constexpr int kLoadSteps = 2;                    // MFMA steps the slice loads are spread over
   auto phase = [&](auto st, int64_t s, auto pending) {
     constexpr int S = decltype(st)::value;
     constexpr bool kPending = decltype(pending)::value;
@@ -314,27 +324,39 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
     read_frags(as, bs, 0, f0);
     if constexpr (kPending) mfma_all(f1);
     dma_all(an, bn, koff);
-    read_frags(as, bs, 1, f1);
-    mfma_all(f0);
-    // Issue order for the scheduler: the next step's fragment reads and the
-    // slice loads spread evenly between the MFMAs.
-    constexpr int kHalf = (kLoads + 1) / 2;
+    static_for<KK - 1>([&](auto t) {
+      constexpr int kk = decltype(t)::value + 1;
+      if constexpr (kk % 2 == 1) {
+        read_frags(as, bs, kk, f1);
+        mfma_all(f0);
+      } else {
+        read_frags(as, bs, kk, f0);
+        mfma_all(f1);
+      }
+    });
+    // Issue order for the scheduler: each step's fragment reads spread between
+    // the previous step's MFMAs, the slice loads between the first two steps'.
     SCHED_DS_READ(kFr);
+    constexpr int v0 = spread(0, kLoads, kLoadSteps);
     if constexpr (kPending) {
       static_for<NMF>([&](auto n) {
-        constexpr int v = spread(decltype(n)::value, kHalf, NMF);
+        constexpr int v = spread(decltype(n)::value, v0, NMF);
         SCHED_MFMA(1);
         if constexpr (v > 0) SCHED_VMEM_READ(v);
       });
     } else {
-      SCHED_VMEM_READ(kHalf);
+      SCHED_VMEM_READ(v0);
     }
-    static_for<NMF>([&](auto n) {
-      constexpr int d = spread(decltype(n)::value, kFr, NMF);
-      constexpr int v = spread(decltype(n)::value, kLoads - kHalf, NMF);
-      SCHED_MFMA(1);
-      if constexpr (d > 0) SCHED_DS_READ(d);
-      if constexpr (v > 0) SCHED_VMEM_READ(v);
+    static_for<KK - 1>([&](auto t) {
+      constexpr int g = decltype(t)::value + 1;
+      constexpr int vg = g < kLoadSteps ? spread(g, kLoads, kLoadSteps) : 0;
+      static_for<NMF>([&](auto n) {
+        constexpr int d = spread(decltype(n)::value, kFr, NMF);
+        constexpr int v = spread(decltype(n)::value, vg, NMF);
+        SCHED_MFMA(1);
+        if constexpr (d > 0) SCHED_DS_READ(d);
+        if constexpr (v > 0) SCHED_VMEM_READ(v);
+      });
     });
     publish_keep(keep_later);
   };
@@ -372,7 +394,7 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
         ++s;
       }
     });
-    mfma_all(f1);  // step (nfull-1, 1)
+    mfma_all(f1);  // step (nfull-1, KK-1)
     // drain the idle reloads before any stage is reused or the workgroup ends
     publish_keep(std::integral_constant<int, 0>{});
   }

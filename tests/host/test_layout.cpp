@@ -42,42 +42,57 @@ static int b128_conflicts(const int* addr) {
   return extra;
 }
 
-int main() {
-  // swizzle: a bijection of the chunks inside every row
-  const int kc = lds_swizzle::kChunks;
+// Both row swizzles: bijective, fragment reads and direct loads conflict-free.
+template <int RowBytes>
+void check_swizzle() {
+  using Z = LdsSwizzle<RowBytes>;
+  const int kc = Z::kChunks;
+  CHECK(kc * 16 == RowBytes, "chunks per row");
   for (int r = 0; r < 256; ++r) {
     std::set<int> seen;
-    for (int c = 0; c < kc; ++c) seen.insert(lds_swizzle::phys_chunk(r, c));
-    CHECK((int)seen.size() == kc, "swizzle not a bijection in row %d", r);
-    for (int c = 0; c < kc; ++c) CHECK(lds_swizzle::logical_chunk(r, lds_swizzle::phys_chunk(r, c)) == c, "inverse");
+    for (int c = 0; c < kc; ++c) seen.insert(Z::phys_chunk(r, c));
+    CHECK((int)seen.size() == kc, "swizzle not a bijection in row %d (%d-byte rows)", r, RowBytes);
+    for (int c = 0; c < kc; ++c) CHECK(Z::logical_chunk(r, Z::phys_chunk(r, c)) == c, "inverse");
+    // the key is a function of the row's low bits only: every 32-row MFMA
+    // tile of a stage sees the same keys
+    CHECK(Z::key(r) == Z::key(r & 31), "key depends on row bits above 4");
   }
   // fragment reads under the measured gfx950 bank model (64 banks x 4 B; a
   // ds_read_b128 serves the 16 lanes with equal (bit5, bit4^bit2) together):
   // lane l reads row base + l%32, logical chunk 2kk + l/32.
   for (int base = 0; base < 256; base += 32)
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kc / 2; ++kk) {
       int addr[64];
-      for (int l = 0; l < 64; ++l) addr[l] = lds_swizzle::offset_bytes(base + (l & 31), 2 * kk + (l >> 5));
-      CHECK(b128_conflicts(addr) == 0, "fragment-read bank conflict base %d kk %d", base, kk);
+      for (int l = 0; l < 64; ++l) addr[l] = Z::offset_bytes(base + (l & 31), 2 * kk + (l >> 5));
+      CHECK(b128_conflicts(addr) == 0, "fragment-read bank conflict base %d kk %d (%d-byte rows)", base, kk,
+            RowBytes);
     }
+  // direct loads: one wavefront writes 1 KiB = 1024/RowBytes whole rows contiguously
+  const int rows = 1024 / RowBytes;
+  for (int r0 = 0; r0 < 256; r0 += rows) {
+    std::set<int> offs;
+    for (int l = 0; l < 64; ++l) offs.insert(Z::offset_bytes(r0 + l / kc, Z::logical_chunk(r0 + l / kc, l % kc)));
+    CHECK(offs.size() == 64 && *offs.begin() == r0 * RowBytes && *offs.rbegin() == r0 * RowBytes + 63 * 16,
+          "direct-load span not contiguous (%d-byte rows)", RowBytes);
+  }
+}
+
+int main() {
+  check_swizzle<64>();
+  check_swizzle<128>();
   // the model reproduces the measured conflicts of unswizzled rows
   {
     int addr[64];
     for (int l = 0; l < 64; ++l) addr[l] = (l & 31) * 64 + 16 * (l >> 5);
     CHECK(b128_conflicts(addr) > 0, "bank model should flag unswizzled 64-byte rows");
+    for (int l = 0; l < 64; ++l) addr[l] = (l & 31) * 128 + 16 * (l >> 5);
+    CHECK(b128_conflicts(addr) > 0, "bank model should flag unswizzled 128-byte rows");
   }
   // direct loads: lane l writes byte 16 l of a 1 KiB span
   {
     int addr[64];
     for (int l = 0; l < 64; ++l) addr[l] = 16 * l;
     CHECK(b128_conflicts(addr) == 0, "direct-load span conflicts");
-  }
-  // direct loads: one wavefront writes 1 KiB = 16 whole rows contiguously
-  for (int r0 = 0; r0 < 256; r0 += 16) {
-    std::set<int> offs;
-    for (int l = 0; l < 64; ++l) offs.insert(lds_swizzle::offset_bytes(r0 + l / kc, lds_swizzle::logical_chunk(r0 + l / kc, l % kc)));
-    CHECK(offs.size() == 64 && *offs.begin() == r0 * lds_swizzle::kRowBytes &&
-          *offs.rbegin() == r0 * lds_swizzle::kRowBytes + 63 * 16, "direct-load span not contiguous");
   }
   // MFMA accumulator maps cover the output tile exactly once
   {
