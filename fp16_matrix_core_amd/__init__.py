@@ -5,7 +5,8 @@ fragment copy runs in the HIP kernels of ``libfp16mc.so``.  PyTorch supplies
 device memory and the current stream; nothing here computes on the CPU, and
 every entry point raises if the library is not built.
 
-    gemm_nt(a, b, out)             Out = A @ B.T  (fp16 in, fp32 out)
+    gemm_nt(a, b, out)             Out = A @ B.T  (fp16 or bf16 in, fp32 or the
+                                   input type out; accumulate=True adds to out)
     gemm_nt_batched(a, b, out)     the same for (batch, M, K) x (batch, N, K)
     frag_copy(src, dst, num, col_major, direction)
     plan(M, N, K, batch=1)         name of the kernel configuration used
@@ -18,10 +19,12 @@ import os
 
 __all__ = [
     "FRAG_LOAD", "FRAG_STORE", "FRAG_ROUNDTRIP", "Fp16mcError", "lib", "lib_path",
-    "gemm_nt", "gemm_nt_batched", "frag_copy", "plan", "gemm_nt_raw", "frag_copy_raw",
+    "gemm_nt", "gemm_nt_batched", "frag_copy", "plan", "gemm_nt_raw", "gemm_nt_ex_raw", "frag_copy_raw",
+    "F32", "F16", "BF16",
 ]
 
 FRAG_LOAD, FRAG_STORE, FRAG_ROUNDTRIP = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
 STATUS = {0: "FP16MC_OK", -1: "FP16MC_EINVAL", -2: "FP16MC_EALIGN", -3: "FP16MC_EHIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +57,8 @@ def lib():
         L.gemm_nt_f16f32.restype = ci
         L.gemm_nt_f16f32_batched.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, vp]
         L.gemm_nt_f16f32_batched.restype = ci
+        L.gemm_nt_ex.argtypes = [vp, vp, vp] + [i64] * 10 + [ci, ci, ci, vp]
+        L.gemm_nt_ex.restype = ci
         L.frag_copy.argtypes = [vp, vp, i64, ci, ci, ci, vp]
         L.frag_copy.restype = ci
         L.gemm_nt_f16f32_plan.argtypes = [i64, i64, i64, i64]
@@ -88,47 +93,78 @@ def gemm_nt_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream=0):
     _check(lib().gemm_nt_f16f32(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream))
 
 
+def gemm_nt_ex_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch=1, sa=0, sb=0, so=0,
+                   ab_type=F16, out_type=F32, accumulate=False, stream=0):
+    """Direct call of gemm_nt_ex with integer device pointers."""
+    _check(lib().gemm_nt_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, sa, sb, so,
+                            ab_type, out_type, int(bool(accumulate)), stream))
+
+
 def frag_copy_raw(src_ptr, dst_ptr, num_tiles, num, col_major, direction, stream=0):
     _check(lib().frag_copy(src_ptr, dst_ptr, num_tiles, num, int(col_major), direction, stream))
 
 
-def gemm_nt(a, b, out=None):
-    """Out = A @ B.T on the GPU. a: (M,K) fp16, b: (N,K) fp16, out: (M,N) fp32 (allocated if None)."""
+def _types(a, b, out_dtype):
     import torch
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("a and b must be float16")
+    codes = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
+        raise TypeError("a and b must both be float16 or both bfloat16")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, a.dtype):
+        raise TypeError("out must be float32 or the inputs' dtype")
+    return codes[a.dtype], codes[out_dtype], out_dtype
+
+
+def gemm_nt(a, b, out=None, accumulate=False, out_dtype=None):
+    """Out = A @ B.T (+ out if accumulate) on the GPU.
+
+    a: (M,K), b: (N,K), both float16 or both bfloat16; out: (M,N) float32 or
+    the inputs' dtype (allocated, with 16-byte-aligned rows, if None; then
+    ``out_dtype`` picks its type and accumulate must be False).
+    """
+    import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form A @ B.T")
     M, K = a.shape
     N = b.shape[0]
     if out is None:
-        # rows padded to a multiple of 4 floats (16-byte aligned rows); a view is returned
-        out = torch.empty((M, N + (-N) % 4), dtype=torch.float32, device=a.device)[:, :N]
-    if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
-        raise ValueError("out must be float32 of shape (M, N)")
-    _check(lib().gemm_nt_f16f32(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
-                                _ld(a, M, K), _ld(b, N, K), _ld(out, M, N), _stream_ptr(a)))
+        if accumulate:
+            raise ValueError("accumulate needs an existing out")
+        ab, ot, odt = _types(a, b, out_dtype)
+        per16 = 16 // torch.empty((), dtype=odt).element_size()
+        out = torch.empty((M, N + (-N) % per16), dtype=odt, device=a.device)[:, :N]
+    else:
+        ab, ot, _ = _types(a, b, out.dtype)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape (M, N)")
+    _check(lib().gemm_nt_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                            _ld(a, M, K), _ld(b, N, K), _ld(out, M, N), 1, 0, 0, 0,
+                            ab, ot, int(bool(accumulate)), _stream_ptr(a)))
     return out
 
 
-def gemm_nt_batched(a, b, out=None):
-    """Batched Out[p] = A[p] @ B[p].T. a: (P,M,K), b: (P,N,K) fp16, out: (P,M,N) fp32."""
+def gemm_nt_batched(a, b, out=None, accumulate=False, out_dtype=None):
+    """Batched Out[p] = A[p] @ B[p].T (+ out[p]). a: (P,M,K), b: (P,N,K); types as gemm_nt."""
     import torch
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("a and b must be float16")
     if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form batched A @ B.T")
     P, M, K = a.shape
     N = b.shape[1]
     if out is None:
-        out = torch.empty((P, M, N + (-N) % 4), dtype=torch.float32, device=a.device)[:, :, :N]
-    if out.dtype != torch.float32 or tuple(out.shape) != (P, M, N):
-        raise ValueError("out must be float32 of shape (P, M, N)")
-    _check(lib().gemm_nt_f16f32_batched(
+        if accumulate:
+            raise ValueError("accumulate needs an existing out")
+        ab, ot, odt = _types(a, b, out_dtype)
+        per16 = 16 // torch.empty((), dtype=odt).element_size()
+        out = torch.empty((P, M, N + (-N) % per16), dtype=odt, device=a.device)[:, :, :N]
+    else:
+        ab, ot, _ = _types(a, b, out.dtype)
+    if tuple(out.shape) != (P, M, N):
+        raise ValueError("out must have shape (P, M, N)")
+    _check(lib().gemm_nt_ex(
         a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
         _ld(a, M, K), _ld(b, N, K), _ld(out, M, N), P,
         a.stride(0) if P > 1 else 0, b.stride(0) if P > 1 else 0, out.stride(0) if P > 1 else 0,
-        _stream_ptr(a)))
+        ab, ot, int(bool(accumulate)), _stream_ptr(a)))
     return out
 
 

@@ -36,9 +36,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // The tile scheduler works in 32-bit arithmetic (grid x group strip < 2^32).
 constexpr int64_t kMaxGrid = int64_t(1) << 28;
 
-int check_gemm(const void* A, const void* B, const float* Out, int64_t M, int64_t N, int64_t K,
+static_assert(static_cast<int>(fp16mc::Dtype::kF32) == FP16MC_F32 &&
+                  static_cast<int>(fp16mc::Dtype::kF16) == FP16MC_F16 &&
+                  static_cast<int>(fp16mc::Dtype::kBF16) == FP16MC_BF16,
+              "internal element-type codes must match fp16mc.h");
+
+int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t sA, int64_t sB,
-               int64_t sO) {
+               int64_t sO, int ab_type, int out_type, int accumulate) {
+  if (ab_type != FP16MC_F16 && ab_type != FP16MC_BF16)
+    return fail(FP16MC_EINVAL, "ab_type=%d must be FP16MC_F16 or FP16MC_BF16", ab_type);
+  if (out_type != FP16MC_F32 && out_type != ab_type)
+    return fail(FP16MC_EINVAL, "out_type=%d must be FP16MC_F32 or the operands' type %d", out_type, ab_type);
+  if (accumulate != 0 && accumulate != 1) return fail(FP16MC_EINVAL, "accumulate must be 0 or 1");
   if (M < 0 || N < 0 || K < 0) return fail(FP16MC_EINVAL, "negative size (M=%lld, N=%lld, K=%lld)",
                                            (long long)M, (long long)N, (long long)K);
   if (batch < 0) return fail(FP16MC_EINVAL, "negative batch %lld", (long long)batch);
@@ -55,10 +65,13 @@ int check_gemm(const void* A, const void* B, const float* Out, int64_t M, int64_
   if ((lda & 7) || (ldb & 7))
     return fail(FP16MC_EALIGN, "lda=%lld and ldb=%lld must be multiples of 8 (16-byte rows)",
                 (long long)lda, (long long)ldb);
-  if (!aligned16(Out) || (ldo & 3))
-    return fail(FP16MC_EALIGN, "Out must be 16-byte aligned and ldo=%lld a multiple of 4", (long long)ldo);
-  if (batch > 1 && ((sA & 7) || (sB & 7) || (sO & 3)))
-    return fail(FP16MC_EALIGN, "batch strides must keep 16-byte alignment (sA, sB %% 8, sO %% 4)");
+  const int64_t per16 = out_type == FP16MC_F32 ? 4 : 8;  // output elements per 16 bytes
+  if (!aligned16(Out) || (ldo % per16))
+    return fail(FP16MC_EALIGN, "Out must be 16-byte aligned and ldo=%lld a multiple of %lld", (long long)ldo,
+                (long long)per16);
+  if (batch > 1 && ((sA & 7) || (sB & 7) || (sO % per16)))
+    return fail(FP16MC_EALIGN, "batch strides must keep 16-byte alignment (sA, sB %% 8, sO %% %lld)",
+                (long long)per16);
   return FP16MC_OK;
 }
 
@@ -66,10 +79,11 @@ int check_gemm(const void* A, const void* B, const float* Out, int64_t M, int64_
 
 extern "C" {
 
-int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
-                           int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA,
-                           int64_t strideB, int64_t strideO, void* stream) {
-  const int rc = check_gemm(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO);
+int gemm_nt_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K, int64_t lda,
+               int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
+               int ab_type, int out_type, int accumulate, void* stream) {
+  const int rc = check_gemm(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO, ab_type,
+                            out_type, accumulate);
   if (rc != FP16MC_OK) return rc;
   const fp16mc::GemmPlan plan = fp16mc::choose_gemm_plan(M, N, K, batch);
   if (plan == fp16mc::GemmPlan::kNone) return ok();
@@ -79,15 +93,25 @@ int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, 
   if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb))
     return fail(FP16MC_EINVAL, "a %s tile of lda=%lld / ldb=%lld rows spans 2^32 bytes or more",
                 fp16mc::gemm_plan_name(plan), (long long)lda, (long long)ldb);
-  fp16mc::GemmProblem p{A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO};
+  fp16mc::GemmProblem p{A,      B,       Out,     M,       N,       K,
+                        lda,    ldb,     ldo,     batch,   strideA, strideB,
+                        strideO, static_cast<fp16mc::Dtype>(ab_type), static_cast<fp16mc::Dtype>(out_type),
+                        accumulate != 0};
   const hipError_t e = fp16mc::launch_gemm(plan, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
+int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
+                           int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA,
+                           int64_t strideB, int64_t strideO, void* stream) {
+  return gemm_nt_ex(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO, FP16MC_F16, FP16MC_F32, 0,
+                    stream);
+}
+
 int gemm_nt_f16f32(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
                    int64_t lda, int64_t ldb, int64_t ldo, void* stream) {
-  return gemm_nt_f16f32_batched(A, B, Out, M, N, K, lda, ldb, ldo, 1, 0, 0, 0, stream);
+  return gemm_nt_ex(A, B, Out, M, N, K, lda, ldb, ldo, 1, 0, 0, 0, FP16MC_F16, FP16MC_F32, 0, stream);
 }
 
 int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_major, int direction,

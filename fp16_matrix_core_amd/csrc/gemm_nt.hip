@@ -47,9 +47,39 @@ namespace fp16mc {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Operand element types.  Both move through the kernels as raw 16-bit
+// patterns; only the matrix instruction that consumes them differs.
+struct InF16 {
+  typedef f16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+struct InBF16 {
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// One output element: the fp32 sum, plus the element's previous value when
+// accumulating, stored as fp32 or rounded to nearest-even fp16 / bf16.
+template <class OutT, bool ACC>
+__device__ __forceinline__ void store_out(OutT* p, float v) {
+  if constexpr (ACC) v += static_cast<float>(*p);
+  *p = static_cast<OutT>(v);
+}
 
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
 // (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
@@ -95,8 +125,8 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 
 
 // Elements [k, k+8) of a row, zero past K.  `row` points at element 0.
 // Only the last, partial K slice of a problem takes this path.
-__device__ __forceinline__ u32x4 load_chunk_masked(const _Float16* row, int64_t k, int64_t K) {
-  const unsigned short* r16 = reinterpret_cast<const unsigned short*>(row);
+__device__ __forceinline__ u32x4 load_chunk_masked(const unsigned short* row, int64_t k, int64_t K) {
+  const unsigned short* r16 = row;
   unsigned int w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -144,9 +174,9 @@ constexpr int spread(int n, int total, int k) { return (n + 1) * total / k - n *
 // s_waitcnt immediate for "vmcnt(n)" with the other counters left alone (gfx9 encoding).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <class C>
+template <class C, class In, class OutT, bool ACC>
 __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD)
-gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, float* __restrict__ Out,
+gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B, OutT* __restrict__ Out,
                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
                int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m, int64_t tiles_n, int64_t total) {
   // One array per (operand, stage): the compiler then knows that the
@@ -198,8 +228,8 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   const int pchunk = lane % C::Swz::kChunks;
   const int64_t a_rows = (M - i0) < C::BM ? (M - i0) : C::BM;
   const int64_t b_rows = (N - j0) < C::BN ? (N - j0) : C::BN;
-  const _Float16* a_tile = A + i0 * lda;
-  const _Float16* b_tile = B + j0 * ldb;
+  const unsigned short* a_tile = A + i0 * lda;
+  const unsigned short* b_tile = B + j0 * ldb;
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_tile, static_cast<unsigned>(2 * ((a_rows - 1) * lda + K)));
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_tile, static_cast<unsigned>(2 * ((b_rows - 1) * ldb + K)));
   unsigned a_off[C::A_LOADS];
@@ -232,13 +262,13 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
-      const _Float16* row = a_tile + a_off[p] / 2 - 8 * lc;
+      const unsigned short* row = a_tile + a_off[p] / 2 - 8 * lc;
       *reinterpret_cast<u32x4*>(as + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
     }
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + prow, pchunk);
-      const _Float16* row = b_tile + b_off[p] / 2 - 8 * lc;
+      const unsigned short* row = b_tile + b_off[p] / 2 - 8 * lc;
       *reinterpret_cast<u32x4*>(bs + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
     }
   };
@@ -261,21 +291,21 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
   static_assert(KK % 2 == 0, "fragments alternate between two register sets");
 
   struct Frags {
-    f16x8 a[C::SI];
-    f16x8 b[C::SJ];
+    typename In::V8 a[C::SI];
+    typename In::V8 b[C::SJ];
   };
   auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) {
     const int pc = ((2 * kk + khalf) ^ key) << 4;
 #pragma unroll
     for (int si = 0; si < C::SI; ++si)
-      f.a[si] = *reinterpret_cast<const f16x8*>(as + a_row0 + si * 32 * C::Swz::kRowBytes + pc);
+      f.a[si] = *reinterpret_cast<const typename In::V8*>(as + a_row0 + si * 32 * C::Swz::kRowBytes + pc);
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj)
-      f.b[sj] = *reinterpret_cast<const f16x8*>(bs + b_row0 + sj * 32 * C::Swz::kRowBytes + pc);
+      f.b[sj] = *reinterpret_cast<const typename In::V8*>(bs + b_row0 + sj * 32 * C::Swz::kRowBytes + pc);
   };
   auto mfma = [&](const Frags& f, int n) {
     const int si = n / C::SJ, sj = n % C::SJ;
-    acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[si], f.b[sj], acc[si][sj], 0, 0, 0);
+    acc[si][sj] = In::mfma32(f.a[si], f.b[sj], acc[si][sj]);
   };
   auto mfma_all = [&](const Frags& f) {
 #pragma unroll
@@ -430,7 +460,7 @@ gemm_nt_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, f
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
-        if (i < M && j < N) Out[i * ldo + j] = acc[si][sj][v];
+        if (i < M && j < N) store_out<OutT, ACC>(Out + i * ldo + j, acc[si][sj][v]);
       }
     }
   }
@@ -457,18 +487,20 @@ constexpr int kSkBlock = 128;      // K per block per wavefront
 
 // Four 16-byte chunks of a row at elements k + 32 j (all inside K).  With
 // k = kb + 8q the four lanes of a row read 64 contiguous bytes per load.
-__device__ __forceinline__ void sk_load(const _Float16* row, int64_t k, u32x4 (&v)[4]) {
+__device__ __forceinline__ void sk_load(const unsigned short* row, int64_t k, u32x4 (&v)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const u32x4*>(row + k + 32 * j);
 }
 // The same with zeros past K (the last, partial block only).
-__device__ __forceinline__ void sk_load_masked(const _Float16* row, int64_t k, int64_t K, u32x4 (&v)[4]) {
+__device__ __forceinline__ void sk_load_masked(const unsigned short* row, int64_t k, int64_t K, u32x4 (&v)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = load_chunk_masked(row, k + 8 * j, K);
 }
 
+template <class In, class OutT, bool ACC>
 __global__ void __launch_bounds__(kSkWaves * 64, 1)
-gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B, float* __restrict__ Out,
+gemm_nt_skinny_kernel(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B,
+                      OutT* __restrict__ Out,
                       int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
                       int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m) {
   __shared__ float red[kSkWaves][kSkRows][16];
@@ -482,7 +514,7 @@ gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict
 
   const int r = mfma16::operand_row(lane);   // row in a 16-row tile / column of B
   const int q = lane >> 4;                   // 32-element quarter of the block
-  const _Float16* arow[4];
+  const unsigned short* arow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t i = i0 + 16 * t + r;
@@ -490,7 +522,7 @@ gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict
   }
   // lanes past N read row N-1 (in bounds) and zero it: no divergent branch
   const bool has_b = r < N;
-  const _Float16* brow = B + (has_b ? r : N - 1) * ldb;
+  const unsigned short* brow = B + (has_b ? r : N - 1) * ldb;
   const unsigned bmask = has_b ? 0xFFFFFFFFu : 0u;
 
   // Full 128-wide K blocks are split evenly over the wavefronts; the last,
@@ -514,10 +546,10 @@ gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict
   auto mma = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f16x8 bj = __builtin_bit_cast(f16x8, vb[buf][j] & bmask);
+      const typename In::V8 bj = __builtin_bit_cast(typename In::V8, vb[buf][j] & bmask);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[buf][t][j]), bj, acc[t], 0, 0, 0);
+        acc[t] = In::mfma16(__builtin_bit_cast(typename In::V8, va[buf][t][j]), bj, acc[t]);
     }
   };
   if (blk0 < blk1) {
@@ -557,7 +589,7 @@ gemm_nt_skinny_kernel(const _Float16* __restrict__ A, const _Float16* __restrict
 #pragma unroll
     for (int w = 0; w < kSkWaves; ++w) sum += red[w][row][col];
     const int64_t i = i0 + row;
-    if (i < M && col < N) Out[i * ldo + col] = sum;
+    if (i < M && col < N) store_out<OutT, ACC>(Out + i * ldo + col, sum);
   }
 }
 
@@ -568,31 +600,63 @@ int64_t tiles_of(int64_t M, int64_t N, int64_t batch, int64_t* tm, int64_t* tn) 
   return *tm * *tn * batch;
 }
 
-template <class C>
+template <class C, class In, class OutT, bool ACC>
 hipError_t launch(const GemmProblem& p, hipStream_t stream) {
   int64_t tm, tn;
   const int64_t total = tiles_of<C>(p.M, p.N, p.batch, &tm, &tn);
-  const _Float16* A = static_cast<const _Float16*>(p.A);
-  const _Float16* B = static_cast<const _Float16*>(p.B);
-  float* Out = p.Out;
+  const unsigned short* A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* B = static_cast<const unsigned short*>(p.B);
+  OutT* Out = static_cast<OutT*>(p.Out);
   int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
   int64_t sA = p.sA, sB = p.sB, sO = p.sO;
   void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tm, &tn,
                   const_cast<int64_t*>(&total)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_kernel<C>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_kernel<C, In, OutT, ACC>),
                          dim3(static_cast<unsigned>(total)), dim3(C::NT), args, 0, stream);
 }
 
+template <class In, class OutT, bool ACC>
 hipError_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
-  const _Float16* A = static_cast<const _Float16*>(p.A);
-  const _Float16* B = static_cast<const _Float16*>(p.B);
-  float* Out = p.Out;
+  const unsigned short* A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* B = static_cast<const unsigned short*>(p.B);
+  OutT* Out = static_cast<OutT*>(p.Out);
   int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
   int64_t sA = p.sA, sB = p.sB, sO = p.sO;
   int64_t tiles_m = (M + kSkRows - 1) / kSkRows;
   void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tiles_m};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_skinny_kernel),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_skinny_kernel<In, OutT, ACC>),
                          dim3(static_cast<unsigned>(tiles_m * p.batch)), dim3(kSkWaves * 64), args, 0, stream);
+}
+
+template <class T>
+struct Tag {
+  typedef T type;
+};
+
+// Calls f(Tag<In>, Tag<OutT>, integral_constant<bool, ACC>) for the problem's types.
+template <class F>
+hipError_t with_types(const GemmProblem& p, F&& f) {
+  std::integral_constant<bool, true> acc;
+  std::integral_constant<bool, false> fresh;
+  if (p.ab_type == Dtype::kBF16) {
+    if (p.out_type == Dtype::kF32) return p.accumulate ? f(Tag<InBF16>{}, Tag<float>{}, acc) : f(Tag<InBF16>{}, Tag<float>{}, fresh);
+    return p.accumulate ? f(Tag<InBF16>{}, Tag<__bf16>{}, acc) : f(Tag<InBF16>{}, Tag<__bf16>{}, fresh);
+  }
+  if (p.out_type == Dtype::kF32) return p.accumulate ? f(Tag<InF16>{}, Tag<float>{}, acc) : f(Tag<InF16>{}, Tag<float>{}, fresh);
+  return p.accumulate ? f(Tag<InF16>{}, Tag<_Float16>{}, acc) : f(Tag<InF16>{}, Tag<_Float16>{}, fresh);
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
+  return with_types(p, [&](auto in, auto out, auto acc) {
+    return launch<C, typename decltype(in)::type, typename decltype(out)::type, decltype(acc)::value>(p, stream);
+  });
+}
+
+hipError_t launch_skinny_typed(const GemmProblem& p, hipStream_t stream) {
+  return with_types(p, [&](auto in, auto out, auto acc) {
+    return launch_skinny<typename decltype(in)::type, typename decltype(out)::type, decltype(acc)::value>(p, stream);
+  });
 }
 
 }  // namespace
@@ -646,10 +710,10 @@ bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb) 
 
 hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream) {
   switch (plan) {
-    case GemmPlan::kWave32: return launch<CfgWave32>(p, stream);
-    case GemmPlan::kWg128x64: return launch<CfgWg128x64>(p, stream);
-    case GemmPlan::kWg256: return launch<CfgWg256>(p, stream);
-    case GemmPlan::kSkinny: return launch_skinny(p, stream);
+    case GemmPlan::kWave32: return launch_cfg<CfgWave32>(p, stream);
+    case GemmPlan::kWg128x64: return launch_cfg<CfgWg128x64>(p, stream);
+    case GemmPlan::kWg256: return launch_cfg<CfgWg256>(p, stream);
+    case GemmPlan::kSkinny: return launch_skinny_typed(p, stream);
     default: return hipSuccess;
   }
 }

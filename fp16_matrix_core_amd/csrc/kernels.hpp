@@ -6,15 +6,23 @@
 
 namespace fp16mc {
 
-// One batched NT product: problem b reads A + b*sA, B + b*sB, writes Out + b*sO.
+// Element types; the values equal fp16mc_dtype of the C header.
+enum class Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// One batched NT product: problem b reads A + b*sA, B + b*sB, writes Out + b*sO
+// (strides in elements).  A and B hold ab_type (F16 or BF16); Out holds
+// out_type (F32 or ab_type); with `accumulate` Out's previous values are added.
 struct GemmProblem {
   const void* A;
   const void* B;
-  float* Out;
+  void* Out;
   int64_t M, N, K;
   int64_t lda, ldb, ldo;
   int64_t batch;
   int64_t sA, sB, sO;
+  Dtype ab_type;
+  Dtype out_type;
+  bool accumulate;
 };
 
 // Kernel configurations, one per shape class.

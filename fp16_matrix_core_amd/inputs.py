@@ -8,7 +8,10 @@ numpy arrays.
 Recipe: numpy ``default_rng(seed)`` (PCG64); uniform draws on [-1, 1] and
 normal draws scaled by 0.1 are made in float64 and rounded to float16
 (round-to-nearest-even); raw bit patterns are uniform over [0, 65536), so NaN,
-infinity, subnormal and -0 patterns occur at their natural rates.
+infinity, subnormal and -0 patterns occur at their natural rates.  bfloat16
+inputs are the same float64 draws rounded to float32 and then to the upper 16
+bits of the float32 pattern, nearest-even; they are returned as uint16 bit
+patterns (numpy has no bfloat16 type).
 """
 
 import numpy as np
@@ -16,7 +19,7 @@ import numpy as np
 __all__ = [
     "uniform_f16", "normal_f16", "random_bits_u16", "identity_f16", "permutation_f16",
     "single_tile", "single_workgroup", "frag_bits", "large_square", "batched_small", "skinny",
-    "FRAG_TILES",
+    "FRAG_TILES", "to_bf16_bits", "uniform_bf16", "normal_bf16", "large_square_bf16", "accumulator_f32",
 ]
 
 FRAG_TILES = 1 << 20   # 8x8 tiles in the fragment-copy workload
@@ -28,6 +31,21 @@ def uniform_f16(shape, rng):
 
 def normal_f16(shape, rng, scale=0.1):
     return (rng.standard_normal(size=shape) * scale).astype(np.float16)
+
+
+def to_bf16_bits(x):
+    """float64/float32 values -> bfloat16 bit patterns (uint16), via float32, nearest-even (finite inputs)."""
+    bits = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def uniform_bf16(shape, rng):
+    return to_bf16_bits(rng.uniform(-1.0, 1.0, size=shape))
+
+
+def normal_bf16(shape, rng, scale=0.1):
+    return to_bf16_bits(rng.standard_normal(size=shape) * scale)
 
 
 def random_bits_u16(n, rng):
@@ -83,3 +101,15 @@ def skinny(m=16384, n=8, k=16384, seed=5):
     """A (m,k), B (n,k), uniform [-1, 1]."""
     rng = np.random.default_rng(seed)
     return uniform_f16((m, k), rng), uniform_f16((n, k), rng)
+
+
+def large_square_bf16(n=8192, seed=6):
+    """The large product with bfloat16 operands: A, B (n, n) ~ N(0,1)*0.1 as bfloat16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    return normal_bf16((n, n), rng), normal_bf16((n, n), rng)
+
+
+def accumulator_f32(shape, seed=7):
+    """Previous output contents for accumulating products: float32 ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(size=shape).astype(np.float32)

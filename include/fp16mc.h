@@ -77,6 +77,52 @@ int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out,
                            int64_t batch, int64_t strideA, int64_t strideB,
                            int64_t strideO, void* stream);
 
+/* Element types of gemm_nt_ex. */
+typedef enum {
+  FP16MC_F32 = 0,  /* IEEE binary32                                        */
+  FP16MC_F16 = 1,  /* IEEE binary16                                        */
+  FP16MC_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32            */
+} fp16mc_dtype;
+
+/*
+ * The general form: `batch` products (as gemm_nt_f16f32_batched) with a
+ * choice of element types and of a fresh or an accumulating output.
+ *
+ *   Out[i*ldo + j] = round_out( sum_{k<K} A[i*lda + k] * B[j*ldb + k]
+ *                               (+ Out[i*ldo + j] when accumulate) )
+ *
+ * ab_type: FP16MC_F16 or FP16MC_BF16, for both A and B -- the float16 and
+ *   bfloat16 forms of the warp matrix instruction ("Warp Matrix
+ *   Instructions", "Other Fragment Shapes and Transfers").  Products are
+ *   exact and summed in fp32 as for gemm_nt_f16f32.
+ * out_type: FP16MC_F32, or the same type as ab_type; a 16-bit output is the
+ *   fp32 result rounded to nearest-even (overflow gives +-inf).
+ * accumulate: 0 -- Out's previous contents are ignored (the first K slice
+ *   starts from zero); 1 -- Out's previous values are read and added before
+ *   the final rounding, i.e. they are the MMA's C operand (the D, A, B, C
+ *   contract of "From Shared Memory to a Matrix Product", whose first issue
+ *   reads C; and "Other TMEM Transfers" on the Blackwell Tensor Cores page,
+ *   accumulators that start from existing values).  With K == 0 an
+ *   accumulating call leaves Out's values unchanged (a 16-bit Out is
+ *   rewritten with the same value).
+ * Result accuracy: every element within 1e-4 * (sum_k |A[i,k]*B[j,k]| plus
+ *   |previous Out| when accumulating) of the exact value, plus half a unit
+ *   in the last place of a 16-bit output format.
+ *
+ * Preconditions and errors are those of gemm_nt_f16f32_batched, with Out's
+ * alignment rule in bytes: Out 16-byte aligned and ldo (and strideO when
+ * batch > 1) a multiple of 16 bytes / element size (4 for fp32, 8 for
+ * 16-bit outputs).  An unknown type, an out_type that is neither F32 nor
+ * ab_type, or accumulate not in {0, 1} is FP16MC_EINVAL.
+ * gemm_nt_f16f32_batched(...) is exactly gemm_nt_ex(..., FP16MC_F16,
+ * FP16MC_F32, 0, stream).
+ */
+int gemm_nt_ex(const void* A, const void* B, void* Out,
+               int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldo,
+               int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
+               int ab_type, int out_type, int accumulate, void* stream);
+
 /* Directions of frag_copy. */
 enum {
   FRAG_LOAD = 0,     /* shared image  -> fragment (the ldmatrix direction)  */

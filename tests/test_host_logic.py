@@ -42,7 +42,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert {"gemm_nt_f16f32", "gemm_nt_f16f32_batched", "frag_copy", "fp16mc_last_error",
+    assert {"gemm_nt_f16f32", "gemm_nt_f16f32_batched", "gemm_nt_ex", "frag_copy", "fp16mc_last_error",
             "gemm_nt_f16f32_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -84,6 +84,42 @@ def test_gemm_batched_validation(L):
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, -1, 0, 0, 0, None) == -1
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 12, 128, 64, None) == -2
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, -8, 128, 64, None) == -1
+
+
+# gemm_nt_ex(A, B, Out, M, N, K, lda, ldb, ldo, batch, sA, sB, sO, ab_type, out_type, accumulate)
+EX_OK = (FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1, 0, 0, 0)
+
+
+@pytest.mark.parametrize("tail,code,needle", [
+    ((0, 0, 0), -1, "ab_type=0"),
+    ((3, 0, 0), -1, "ab_type=3"),
+    ((1, 2, 0), -1, "out_type=2"),
+    ((2, 1, 0), -1, "out_type=1"),
+    ((1, 0, 2), -1, "accumulate"),
+    ((1, 0, -1), -1, "accumulate"),
+])
+def test_gemm_ex_type_validation(L, tail, code, needle):
+    assert L.gemm_nt_ex(*EX_OK, *tail, None) == code
+    assert needle in L.fp16mc_last_error().decode()
+
+
+def test_gemm_ex_output_alignment_follows_the_output_type(L):
+    # ldo = 12: a multiple of 4 (16 bytes of fp32) but not of 8 (16 bytes of fp16 / bf16)
+    base = (FAKE, FAKE, FAKE, 8, 12, 16, 16, 16, 12, 1, 0, 0, 0)
+    for ab, out in ((1, 1), (2, 2)):
+        assert L.gemm_nt_ex(*base, ab, out, 0, None) == -2
+        assert "multiple of 8" in L.fp16mc_last_error().decode()
+    # batched: strideO must be a multiple of 8 for 16-bit outputs
+    assert L.gemm_nt_ex(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 128, 128, 68, 1, 1, 1, None) == -2
+    # the old entry points are gemm_nt_ex(F16, F32, fresh): same checks, same codes
+    assert L.gemm_nt_ex(*EX_OK[:8], 4, 1, 0, 0, 0, 1, 0, 0, None) == -1
+    assert L.gemm_nt_f16f32(*EX_OK[:8], 4, None) == -1
+
+
+def test_gemm_ex_empty_problems(L):
+    for ab, out, acc in ((1, 0, 0), (1, 1, 1), (2, 0, 1), (2, 2, 0)):
+        assert L.gemm_nt_ex(0, 0, 0, 0, 8, 16, 16, 16, 8, 1, 0, 0, 0, ab, out, acc, None) == 0
+        assert L.gemm_nt_ex(0, 0, 0, 8, 8, 16, 16, 16, 8, 0, 0, 0, 0, ab, out, acc, None) == 0
 
 
 def test_empty_problems_enqueue_nothing(L):

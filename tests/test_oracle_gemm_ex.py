@@ -1,0 +1,228 @@
+"""Pins of oracle.gemm_ex (bfloat16 operands, accumulation, 16-bit outputs).
+
+Each pin ties the oracle to something other than itself: the binary32 /
+bfloat16 format definitions, an independent library conversion (torch on the
+CPU), exact small-integer arithmetic, closed forms, and planted mistakes that
+must fail the acceptance rule.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import gemm as og
+from oracle import gemm_ex as ox
+from fp16_matrix_core_amd import inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---- bfloat16 decoding ------------------------------------------------------------
+
+# Patterns fixed by the formats: bfloat16 is the upper half of a binary32
+# (sign bit, 8 exponent bits with bias 127, 7 stored significand bits).
+BF16_PATTERNS = [
+    (0x0000, 0.0), (0x8000, -0.0), (0x3F80, 1.0), (0xBF80, -1.0), (0x4000, 2.0), (0xC000, -2.0),
+    (0x3F00, 0.5), (0x4049, 3.140625), (0x3FC0, 1.5), (0x7F7F, 3.3895313892515355e38),
+    (0x0080, 2.0 ** -126), (0x0001, 2.0 ** -133), (0x807F, -(127 * 2.0 ** -133)),
+    (0x7F80, np.inf), (0xFF80, -np.inf),
+]
+
+
+def test_bf16_decode_format_patterns():
+    bits = np.array([p for p, _ in BF16_PATTERNS], dtype=np.uint16)
+    got = ox.bf16_to_f64(bits)
+    for (p, want), g in zip(BF16_PATTERNS, got):
+        assert g == want and np.signbit(g) == np.signbit(want), hex(p)
+    nan = ox.bf16_to_f64(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16))
+    assert np.isnan(nan).all()
+
+
+def test_bf16_decode_matches_torch_on_all_patterns():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = ox.bf16_to_f64(bits)
+    theirs = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (ours == theirs) | (np.isnan(ours) & np.isnan(theirs))
+    assert same.all()
+
+
+def test_operand_formats_are_checked():
+    with pytest.raises(TypeError):
+        ox.operand_f64(np.zeros(4, np.float32), "f16")
+    with pytest.raises(TypeError):
+        ox.operand_f64(np.zeros(4, np.float16), "bf16")
+    with pytest.raises(ValueError):
+        ox.operand_f64(np.zeros(4, np.float16), "f8")
+
+
+# ---- the product with bfloat16 operands -------------------------------------------
+
+def _loops(a, b):
+    M, K = a.shape
+    N = b.shape[0]
+    ref = np.zeros((M, N))
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += a[i, k] * b[j, k]
+            ref[i, j] = s
+    return ref
+
+
+def test_bf16_product_library_step_matches_loops():
+    rng = np.random.default_rng(11)
+    for (M, N, K) in [(1, 1, 1), (5, 3, 7), (16, 8, 16), (9, 17, 33)]:
+        A = inputs.uniform_bf16((M, K), rng)
+        B = inputs.uniform_bf16((N, K), rng)
+        ref, bound = ox.gemm_nt_ex(A, B, ab="bf16")
+        a, b = ox.bf16_to_f64(A), ox.bf16_to_f64(B)
+        assert np.array_equal(ref, _loops(a, b))
+        assert np.array_equal(bound, _loops(np.abs(a), np.abs(b)))
+
+
+def test_bf16_identity_and_permutation_closed_forms():
+    rng = np.random.default_rng(12)
+    A = inputs.uniform_bf16((8, 32), rng)
+    eye = inputs.to_bf16_bits(np.eye(32))
+    ref, _ = ox.gemm_nt_ex(A, eye, ab="bf16")
+    assert np.array_equal(ref, ox.bf16_to_f64(A))
+    perm = np.random.default_rng(13).permutation(32)
+    P = np.zeros((32, 32))
+    P[np.arange(32), perm] = 1.0
+    ref, _ = ox.gemm_nt_ex(A, inputs.to_bf16_bits(P), ab="bf16")
+    assert np.array_equal(ref, ox.bf16_to_f64(A)[:, perm])
+
+
+def test_bf16_small_integers_exact():
+    # integers up to 2^8 are exact in bfloat16; their products sum exactly in float64
+    rng = np.random.default_rng(14)
+    a = rng.integers(-16, 17, size=(6, 40)).astype(np.float64)
+    b = rng.integers(-16, 17, size=(5, 40)).astype(np.float64)
+    ref, _ = ox.gemm_nt_ex(inputs.to_bf16_bits(a), inputs.to_bf16_bits(b), ab="bf16")
+    assert np.array_equal(ref, a @ b.T)
+
+
+def test_f16_path_equals_the_plain_oracle():
+    rng = np.random.default_rng(15)
+    A = inputs.uniform_f16((33, 70), rng)
+    B = inputs.uniform_f16((21, 70), rng)
+    r1, b1 = ox.gemm_nt_ex(A, B, ab="f16")
+    r2, b2 = og.gemm_nt(A, B)
+    assert np.array_equal(r1, r2) and np.array_equal(b1, b2)
+
+
+# ---- accumulation ---------------------------------------------------------------------
+
+def test_accumulate_with_zero_operands_returns_c():
+    C = inputs.accumulator_f32((7, 9), seed=16)
+    A = np.zeros((7, 12), np.float16)
+    B = inputs.uniform_f16((9, 12), np.random.default_rng(16))
+    ref, bound = ox.gemm_nt_ex(A, B, C)
+    assert np.array_equal(ref, C.astype(np.float64))
+    assert np.array_equal(bound, np.abs(C.astype(np.float64)))
+
+
+def test_accumulate_is_c_plus_product_exactly_on_integers():
+    rng = np.random.default_rng(17)
+    a = rng.integers(-8, 9, size=(4, 24)).astype(np.float16)
+    b = rng.integers(-8, 9, size=(6, 24)).astype(np.float16)
+    c = rng.integers(-100, 101, size=(4, 6)).astype(np.float32)
+    ref, _ = ox.gemm_nt_ex(a, b, c)
+    assert np.array_equal(ref, a.astype(np.float64) @ b.astype(np.float64).T + c)
+    # C given as float16 or as bfloat16 patterns decodes to the same values
+    r16, _ = ox.gemm_nt_ex(a, b, c.astype(np.float16), c_fmt="f16")
+    rbf, _ = ox.gemm_nt_ex(a, b, inputs.to_bf16_bits(c), c_fmt="bf16")
+    assert np.array_equal(r16, ref) and np.array_equal(rbf, ref)
+
+
+def test_accumulate_planted_mistakes_fail():
+    rng = np.random.default_rng(18)
+    A = inputs.uniform_f16((16, 64), rng)
+    B = inputs.uniform_f16((16, 64), rng)
+    C = inputs.accumulator_f32((16, 16), seed=18)
+    ref, bound = ox.gemm_nt_ex(A, B, C)
+    ref0, _ = og.gemm_nt(A, B)
+    # C dropped, C subtracted, C added twice: all fail
+    for wrong in (ref0, ref0 - C, ref0 + 2 * C.astype(np.float64)):
+        assert not ox.within_bound_out(wrong, ref, bound, "f32")[0]
+    assert ox.within_bound_out(ref.astype(np.float32), ref, bound, "f32")[0]
+
+
+# ---- 16-bit outputs ------------------------------------------------------------------
+
+def test_half_ulp_values_from_the_formats():
+    assert ox.half_ulp(1.0, "f16") == 2.0 ** -11
+    assert ox.half_ulp(1.999, "f16") == 2.0 ** -11
+    assert ox.half_ulp(2.0, "f16") == 2.0 ** -10
+    assert ox.half_ulp(65504.0, "f16") == 16.0
+    assert ox.half_ulp(2.0 ** -20, "f16") == 2.0 ** -25    # subnormal spacing 2^-24
+    assert ox.half_ulp(0.0, "f16") == 2.0 ** -25
+    assert ox.half_ulp(1.0, "bf16") == 2.0 ** -8
+    assert ox.half_ulp(-3.0, "bf16") == 2.0 ** -7
+    assert ox.half_ulp(2.0 ** -130, "bf16") == 2.0 ** -134
+    assert ox.half_ulp(123.0, "f32") == 0.0
+
+
+def test_half_ulp_bounds_numpy_float16_rounding_and_is_tight():
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-26, 15, 200000))
+    x = x[np.abs(x) < 65504]
+    err = np.abs(x.astype(np.float16).astype(np.float64) - x)
+    assert (err <= ox.half_ulp(x, "f16")).all()
+    mid = np.array([1.0 + 2.0 ** -11, 3.0 * 2.0 ** -25, 1024.0 + 0.5])  # exact midpoints
+    err = np.abs(mid.astype(np.float16).astype(np.float64) - mid)
+    assert np.array_equal(err, ox.half_ulp(mid, "f16"))
+
+
+def test_half_ulp_bounds_torch_bfloat16_rounding_and_is_tight():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(20)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-130, 100, 200000))).astype(np.float32)
+    r = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    x64 = x.astype(np.float64)
+    ok = np.isfinite(r)
+    assert (np.abs(r - x64)[ok] <= ox.half_ulp(x64, "bf16")[ok]).all()
+    mid = np.array([1.0 + 2.0 ** -8, 3.0 * 2.0 ** -134], dtype=np.float32)
+    r = torch.from_numpy(mid).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(np.abs(r - mid.astype(np.float64)), ox.half_ulp(mid.astype(np.float64), "bf16"))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_rounded_output_passes_and_planted_mistakes_fail(fmt):
+    rng = np.random.default_rng(21)
+    if fmt == "f16":
+        A, B = inputs.uniform_f16((24, 64), rng), inputs.uniform_f16((20, 64), rng)
+        a, b = A.astype(np.float64), B.astype(np.float64)
+        rnd = lambda v: np.asarray(v).astype(np.float16).astype(np.float64)  # noqa: E731
+    else:
+        A, B = inputs.uniform_bf16((24, 64), rng), inputs.uniform_bf16((20, 64), rng)
+        a, b = ox.bf16_to_f64(A), ox.bf16_to_f64(B)
+        rnd = lambda v: ox.bf16_to_f64(inputs.to_bf16_bits(v))  # noqa: E731
+    ref, bound = ox.gemm_nt_ex(A, B, ab=fmt)
+    # the correctly rounded fp32 sum passes
+    assert ox.within_bound_out(rnd(ref.astype(np.float32)), ref, bound, fmt)[0]
+    # dropped last term, wrong sign of a term, K shifted by one, transposed operand
+    dropped = a[:, :-1] @ b[:, :-1].T
+    sign = ref - 2 * np.outer(a[:, 5], b[:, 5])
+    shifted = a[:, 1:] @ b[:, :-1].T
+    for wrong in (dropped, sign, shifted):
+        assert not ox.within_bound_out(rnd(wrong), ref, bound, fmt)[0]
+    sq_ref, sq_bound = ox.gemm_nt_ex(A[:20], B, ab=fmt)
+    assert not ox.within_bound_out(rnd(sq_ref.T), sq_ref, sq_bound, fmt)[0]
+    # non-finite values fail
+    bad = rnd(ref.astype(np.float32))
+    bad[3, 4] = np.nan
+    assert not ox.within_bound_out(bad, ref, bound, fmt)[0]
+
+
+def test_fp32_rule_unchanged_for_f32_outputs():
+    rng = np.random.default_rng(22)
+    A, B = inputs.uniform_f16((10, 50), rng), inputs.uniform_f16((12, 50), rng)
+    ref, bound = og.gemm_nt(A, B)
+    out = ref.astype(np.float32)
+    for o in (out, out + 1e-3):
+        ok1, worst1, nbad1 = og.within_bound(o, ref, bound)
+        ok2, worst2, nbad2 = ox.within_bound_out(o, ref, bound, "f32")
+        assert (ok1, nbad1) == (ok2, nbad2)
+        assert worst2 == pytest.approx(worst1 / 1e-4)   # worst is measured against the allowance
