@@ -184,6 +184,36 @@ def bench_skinny(torch, f, stream, reps=20):
             "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
+def bench_types(torch, f, stream, a, b, reps=20):
+    """The 8192^3 launch with bfloat16 operands, 16-bit outputs and accumulation (gemm_nt_ex)."""
+    from fp16_matrix_core_amd import inputs
+    n = 8192
+    A16, B16 = inputs.large_square_bf16(n)
+    abf = torch.from_numpy(A16.view("int16")).cuda()
+    bbf = torch.from_numpy(B16.view("int16")).cuda()
+    outs = {"f32": torch.zeros((n, n), dtype=torch.float32, device="cuda"),
+            "f16": torch.zeros((n, n), dtype=torch.float16, device="cuda"),
+            "bf16": torch.zeros((n, n), dtype=torch.bfloat16, device="cuda")}
+    code = {"f32": f.F32, "f16": f.F16, "bf16": f.BF16}
+    res = {}
+    for name, (x, y, ab, ot, acc) in {
+            "bf16_in_f32_out": (abf, bbf, "bf16", "f32", False),
+            "bf16_in_bf16_out": (abf, bbf, "bf16", "bf16", False),
+            "f16_in_f16_out": (a, b, "f16", "f16", False),
+            "f16_in_f32_out_accumulate": (a, b, "f16", "f32", True)}.items():
+        o = outs[ot]
+
+        def call():
+            f.gemm_nt_ex_raw(x.data_ptr(), y.data_ptr(), o.data_ptr(), n, n, n, n, n, n, 1, 0, 0, 0,
+                             code[ab], code[ot], acc, stream.cuda_stream)
+        for _ in range(20):
+            call()
+        ms = StreamTimer(torch, stream).time(call, reps)
+        tf = 2.0 * n ** 3 / ms / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_TFLOPS, 4)}
+    return res
+
+
 def pmc_pass(torch, f):
     """Three 8192^3 launches, then three copies of 1 GiB (the counter calibration kernel)."""
     from fp16_matrix_core_amd import inputs
@@ -272,10 +302,11 @@ def main():
                      "kernel": plan, "us_per_launch": round(ms_event * 1e3, 2), "source_hash": khash},
     }
     if not args.no_secondary:
-        log("secondary: frag_copy, batched, skinny")
+        log("secondary: frag_copy, batched, skinny, operand/output types")
         result["secondary"] = {"frag_copy": bench_frag(torch, f, stream),
                                "batched_4096x128x64x64": bench_batched(torch, f, stream),
-                               "skinny_16384x8x16384": bench_skinny(torch, f, stream)}
+                               "skinny_16384x8x16384": bench_skinny(torch, f, stream),
+                               "gemm_8192_types": bench_types(torch, f, stream, a, b)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(A, B)

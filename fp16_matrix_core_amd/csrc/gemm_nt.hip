@@ -451,16 +451,32 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
 
   // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
   // i = i0 + wm*WTM + 32 si + 8(v/4) + 4(l/32) + v%4, j = j0 + wn*WTN + 32 sj + l%32:
-  // one dword store per v writes two whole 128-byte row segments.
+  // one dword store per v writes two whole 128-byte row segments.  When
+  // accumulating, a row block's previous values are all loaded before any of
+  // its stores (ldo is a run-time value, so the compiler cannot prove that a
+  // store does not alias a later load and would otherwise wait on each load).
 #pragma unroll
   for (int si = 0; si < C::SI; ++si) {
+    float prev[C::SJ][16];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int sj = 0; sj < C::SJ; ++sj) {
+        const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+          prev[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj) {
       const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
-        if (i < M && j < N) store_out<OutT, ACC>(Out + i * ldo + j, acc[si][sj][v]);
+        const float val = ACC ? acc[si][sj][v] + prev[sj][v] : acc[si][sj][v];
+        if (i < M && j < N) Out[i * ldo + j] = static_cast<OutT>(val);
       }
     }
   }
