@@ -35,8 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fp16 NT GEMM TFLOP/s (fp32 acc) at 8192^3; % of MFMA fp16 peak"
 PEAK_TFLOPS = 2516.6       # MI355X dense fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-GEMM_SOURCES = ["fp16_matrix_core_amd/csrc/gemm_nt.hip", "fp16_matrix_core_amd/csrc/layout.hpp",
-                "fp16_matrix_core_amd/csrc/kernels.hpp"]
+GEMM_SOURCES = ["fp16_matrix_core_amd/csrc/gemm_kernels.hpp", "fp16_matrix_core_amd/csrc/gemm_nt.hip",
+                "fp16_matrix_core_amd/csrc/layout.hpp", "fp16_matrix_core_amd/csrc/kernels.hpp"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.txt")
 
 
@@ -214,6 +214,31 @@ def bench_types(torch, f, stream, a, b, reps=20):
     return res
 
 
+def bench_layouts(torch, f, stream, A, B, reps=20):
+    """The 8192^3 fp16 -> fp32 launch with operands stored with K indexing their rows (gemm_ex)."""
+    import numpy as np
+    n = 8192
+    a_mk = torch.from_numpy(A).cuda()
+    b_nk = torch.from_numpy(B).cuda()
+    a_km = torch.from_numpy(np.ascontiguousarray(A.T)).cuda()
+    b_kn = torch.from_numpy(np.ascontiguousarray(B.T)).cuda()
+    o = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, (x, y, ao, bo) in {"nn_b_stored_KxN": (a_mk, b_kn, f.K_CONTIGUOUS, f.MN_CONTIGUOUS),
+                                 "tt_a_stored_KxM": (a_km, b_nk, f.MN_CONTIGUOUS, f.K_CONTIGUOUS),
+                                 "tn_both_stored_Kx": (a_km, b_kn, f.MN_CONTIGUOUS, f.MN_CONTIGUOUS)}.items():
+        def call():
+            f.gemm_ex_raw(x.data_ptr(), y.data_ptr(), o.data_ptr(), n, n, n, n, n, n, 1, 0, 0, 0,
+                          ao, bo, f.F16, f.F32, False, stream.cuda_stream)
+        for _ in range(20):
+            call()
+        ms = StreamTimer(torch, stream).time(call, reps)
+        tf = 2.0 * n ** 3 / ms / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_TFLOPS, 4)}
+    del a_km, b_kn
+    return res
+
+
 def pmc_pass(torch, f):
     """Three 8192^3 launches, then three copies of 1 GiB (the counter calibration kernel)."""
     from fp16_matrix_core_amd import inputs
@@ -302,11 +327,12 @@ def main():
                      "kernel": plan, "us_per_launch": round(ms_event * 1e3, 2), "source_hash": khash},
     }
     if not args.no_secondary:
-        log("secondary: frag_copy, batched, skinny, operand/output types")
+        log("secondary: frag_copy, batched, skinny, operand/output types, storage orders")
         result["secondary"] = {"frag_copy": bench_frag(torch, f, stream),
                                "batched_4096x128x64x64": bench_batched(torch, f, stream),
                                "skinny_16384x8x16384": bench_skinny(torch, f, stream),
-                               "gemm_8192_types": bench_types(torch, f, stream, a, b)}
+                               "gemm_8192_types": bench_types(torch, f, stream, a, b),
+                               "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(A, B)

@@ -8,6 +8,9 @@ every entry point raises if the library is not built.
     gemm_nt(a, b, out)             Out = A @ B.T  (fp16 or bf16 in, fp32 or the
                                    input type out; accumulate=True adds to out)
     gemm_nt_batched(a, b, out)     the same for (batch, M, K) x (batch, N, K)
+    matmul(a, b, out)              Out = a @ b for (M,K) x (K,N) views with any
+                                   contiguous dimension (the storage order of
+                                   each operand is read from its strides)
     frag_copy(src, dst, num, col_major, direction)
     plan(M, N, K, batch=1)         name of the kernel configuration used
 
@@ -20,11 +23,12 @@ import os
 __all__ = [
     "FRAG_LOAD", "FRAG_STORE", "FRAG_ROUNDTRIP", "Fp16mcError", "lib", "lib_path",
     "gemm_nt", "gemm_nt_batched", "frag_copy", "plan", "gemm_nt_raw", "gemm_nt_ex_raw", "frag_copy_raw",
-    "F32", "F16", "BF16",
+    "F32", "F16", "BF16", "K_CONTIGUOUS", "MN_CONTIGUOUS", "matmul", "gemm_ex_raw", "plan_ex",
 ]
 
 FRAG_LOAD, FRAG_STORE, FRAG_ROUNDTRIP = 0, 1, 2
 F32, F16, BF16 = 0, 1, 2
+K_CONTIGUOUS, MN_CONTIGUOUS = 0, 1
 STATUS = {0: "FP16MC_OK", -1: "FP16MC_EINVAL", -2: "FP16MC_EALIGN", -3: "FP16MC_EHIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +63,10 @@ def lib():
         L.gemm_nt_f16f32_batched.restype = ci
         L.gemm_nt_ex.argtypes = [vp, vp, vp] + [i64] * 10 + [ci, ci, ci, vp]
         L.gemm_nt_ex.restype = ci
+        L.gemm_ex.argtypes = [vp, vp, vp] + [i64] * 10 + [ci, ci, ci, ci, ci, vp]
+        L.gemm_ex.restype = ci
+        L.gemm_ex_plan.argtypes = [i64, i64, i64, i64, ci, ci]
+        L.gemm_ex_plan.restype = ctypes.c_char_p
         L.frag_copy.argtypes = [vp, vp, i64, ci, ci, ci, vp]
         L.frag_copy.restype = ci
         L.gemm_nt_f16f32_plan.argtypes = [i64, i64, i64, i64]
@@ -98,6 +106,14 @@ def gemm_nt_ex_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch=1, sa=0,
     """Direct call of gemm_nt_ex with integer device pointers."""
     _check(lib().gemm_nt_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, sa, sb, so,
                             ab_type, out_type, int(bool(accumulate)), stream))
+
+
+def gemm_ex_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch=1, sa=0, sb=0, so=0,
+                a_order=K_CONTIGUOUS, b_order=K_CONTIGUOUS, ab_type=F16, out_type=F32, accumulate=False,
+                stream=0):
+    """Direct call of gemm_ex with integer device pointers."""
+    _check(lib().gemm_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, sa, sb, so,
+                         a_order, b_order, ab_type, out_type, int(bool(accumulate)), stream))
 
 
 def frag_copy_raw(src_ptr, dst_ptr, num_tiles, num, col_major, direction, stream=0):
@@ -168,6 +184,51 @@ def gemm_nt_batched(a, b, out=None, accumulate=False, out_dtype=None):
     return out
 
 
+def _order(t, contiguous_dim):
+    """(storage order, leading dimension) of a 2-D operand view.
+
+    ``contiguous_dim`` is the view dimension that indexes K.  A view whose K
+    dimension has stride 1 is K-contiguous; one whose other dimension has
+    stride 1 is stored with K indexing its rows.
+    """
+    other = 1 - contiguous_dim
+    rows_k, rows_o = t.shape[contiguous_dim], t.shape[other]
+    if t.stride(contiguous_dim) == 1 or rows_k <= 1:
+        return K_CONTIGUOUS, (t.stride(other) if rows_o > 1 else max(rows_k, 1) + (-max(rows_k, 1)) % 8)
+    if t.stride(other) == 1 or rows_o <= 1:
+        return MN_CONTIGUOUS, (t.stride(contiguous_dim) if rows_k > 1 else max(rows_o, 1) + (-max(rows_o, 1)) % 8)
+    raise ValueError("operand views need one dimension with stride 1")
+
+
+def matmul(a, b, out=None, accumulate=False, out_dtype=None):
+    """Out = a @ b (+ out if accumulate) for a (M, K) and b (K, N) views.
+
+    Either operand may be K-contiguous or stored with K indexing its rows
+    (e.g. ``x.t()`` of a row-major tensor); the storage order is read from the
+    strides.  Types as gemm_nt.
+    """
+    import torch
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form a @ b")
+    M, K = a.shape
+    N = b.shape[1]
+    a_order, lda = _order(a, 1)
+    b_order, ldb = _order(b, 0)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out")
+        ab, ot, odt = _types(a, b, out_dtype)
+        per16 = 16 // torch.empty((), dtype=odt).element_size()
+        out = torch.empty((M, N + (-N) % per16), dtype=odt, device=a.device)[:, :N]
+    else:
+        ab, ot, _ = _types(a, b, out.dtype)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape (M, N)")
+    _check(lib().gemm_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, _ld(out, M, N),
+                         1, 0, 0, 0, a_order, b_order, ab, ot, int(bool(accumulate)), _stream_ptr(a)))
+    return out
+
+
 def frag_copy(src, dst, num, col_major, direction):
     """Fragment copy between two contiguous device buffers of num_tiles * 128 bytes each."""
     if not (src.is_contiguous() and dst.is_contiguous()):
@@ -182,4 +243,9 @@ def frag_copy(src, dst, num, col_major, direction):
 
 def plan(M, N, K, batch=1):
     name = lib().gemm_nt_f16f32_plan(M, N, K, batch)
+    return name.decode() if name is not None else None
+
+
+def plan_ex(M, N, K, batch=1, a_order=K_CONTIGUOUS, b_order=K_CONTIGUOUS):
+    name = lib().gemm_ex_plan(M, N, K, batch, a_order, b_order)
     return name.decode() if name is not None else None

@@ -43,7 +43,11 @@ static_assert(static_cast<int>(fp16mc::Dtype::kF32) == FP16MC_F32 &&
 
 int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int64_t ldo, int64_t batch, int64_t sA, int64_t sB,
-               int64_t sO, int ab_type, int out_type, int accumulate) {
+               int64_t sO, int a_order, int b_order, int ab_type, int out_type, int accumulate) {
+  if ((a_order != FP16MC_K_CONTIGUOUS && a_order != FP16MC_MN_CONTIGUOUS) ||
+      (b_order != FP16MC_K_CONTIGUOUS && b_order != FP16MC_MN_CONTIGUOUS))
+    return fail(FP16MC_EINVAL, "a_order=%d and b_order=%d must be FP16MC_K_CONTIGUOUS or FP16MC_MN_CONTIGUOUS",
+                a_order, b_order);
   if (ab_type != FP16MC_F16 && ab_type != FP16MC_BF16)
     return fail(FP16MC_EINVAL, "ab_type=%d must be FP16MC_F16 or FP16MC_BF16", ab_type);
   if (out_type != FP16MC_F32 && out_type != ab_type)
@@ -52,8 +56,11 @@ int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t
   if (M < 0 || N < 0 || K < 0) return fail(FP16MC_EINVAL, "negative size (M=%lld, N=%lld, K=%lld)",
                                            (long long)M, (long long)N, (long long)K);
   if (batch < 0) return fail(FP16MC_EINVAL, "negative batch %lld", (long long)batch);
-  if (lda < K) return fail(FP16MC_EINVAL, "lda=%lld < K=%lld", (long long)lda, (long long)K);
-  if (ldb < K) return fail(FP16MC_EINVAL, "ldb=%lld < K=%lld", (long long)ldb, (long long)K);
+  const bool a_mn = a_order == FP16MC_MN_CONTIGUOUS, b_mn = b_order == FP16MC_MN_CONTIGUOUS;
+  if (!a_mn && lda < K) return fail(FP16MC_EINVAL, "lda=%lld < K=%lld", (long long)lda, (long long)K);
+  if (a_mn && lda < M) return fail(FP16MC_EINVAL, "lda=%lld < M=%lld (A stored K x M)", (long long)lda, (long long)M);
+  if (!b_mn && ldb < K) return fail(FP16MC_EINVAL, "ldb=%lld < K=%lld", (long long)ldb, (long long)K);
+  if (b_mn && ldb < N) return fail(FP16MC_EINVAL, "ldb=%lld < N=%lld (B stored K x N)", (long long)ldb, (long long)N);
   if (ldo < N) return fail(FP16MC_EINVAL, "ldo=%lld < N=%lld", (long long)ldo, (long long)N);
   if (sA < 0 || sB < 0 || sO < 0) return fail(FP16MC_EINVAL, "negative batch stride");
   const bool live = M > 0 && N > 0 && batch > 0;
@@ -79,27 +86,35 @@ int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t
 
 extern "C" {
 
-int gemm_nt_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K, int64_t lda,
-               int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
-               int ab_type, int out_type, int accumulate, void* stream) {
-  const int rc = check_gemm(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO, ab_type,
-                            out_type, accumulate);
+int gemm_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+            int64_t ldo, int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO, int a_order,
+            int b_order, int ab_type, int out_type, int accumulate, void* stream) {
+  const int rc = check_gemm(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO, a_order,
+                            b_order, ab_type, out_type, accumulate);
   if (rc != FP16MC_OK) return rc;
-  const fp16mc::GemmPlan plan = fp16mc::choose_gemm_plan(M, N, K, batch);
+  const bool a_mn = a_order == FP16MC_MN_CONTIGUOUS, b_mn = b_order == FP16MC_MN_CONTIGUOUS;
+  const fp16mc::GemmPlan plan = fp16mc::choose_gemm_plan(M, N, K, batch, a_mn, b_mn);
   if (plan == fp16mc::GemmPlan::kNone) return ok();
   const int64_t grid = fp16mc::gemm_plan_grid(plan, M, N, batch);
   if (grid > kMaxGrid) return fail(FP16MC_EINVAL, "problem needs %lld workgroups (limit %lld)",
                                    (long long)grid, (long long)kMaxGrid);
-  if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb))
+  if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb, a_mn, b_mn))
     return fail(FP16MC_EINVAL, "a %s tile of lda=%lld / ldb=%lld rows spans 2^32 bytes or more",
                 fp16mc::gemm_plan_name(plan), (long long)lda, (long long)ldb);
   fp16mc::GemmProblem p{A,      B,       Out,     M,       N,       K,
                         lda,    ldb,     ldo,     batch,   strideA, strideB,
                         strideO, static_cast<fp16mc::Dtype>(ab_type), static_cast<fp16mc::Dtype>(out_type),
-                        accumulate != 0};
+                        accumulate != 0, a_mn, b_mn};
   const hipError_t e = fp16mc::launch_gemm(plan, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int gemm_nt_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K, int64_t lda,
+               int64_t ldb, int64_t ldo, int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
+               int ab_type, int out_type, int accumulate, void* stream) {
+  return gemm_ex(A, B, Out, M, N, K, lda, ldb, ldo, batch, strideA, strideB, strideO, FP16MC_K_CONTIGUOUS,
+                 FP16MC_K_CONTIGUOUS, ab_type, out_type, accumulate, stream);
 }
 
 int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out, int64_t M, int64_t N, int64_t K,
@@ -134,7 +149,12 @@ int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_ma
 }
 
 const char* gemm_nt_f16f32_plan(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch));
+  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, false, false));
+}
+
+const char* gemm_ex_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int a_order, int b_order) {
+  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, a_order == FP16MC_MN_CONTIGUOUS,
+                                                         b_order == FP16MC_MN_CONTIGUOUS));
 }
 
 const char* fp16mc_last_error(void) { return g_err; }

@@ -1,0 +1,813 @@
+// gemm_kernels.hpp -- Out = A @ B.T on gfx950: the kernel templates.
+// Each storage order of the operands is instantiated in a source file of its
+// own (gemm_nt.hip, gemm_nn.hip, gemm_tt.hip, gemm_tn.hip) so that they
+// compile in parallel; gemm_plan.hip holds the host-side plan logic.
+//
+// The operation is the one "Warp Matrix Instructions" and "Blackwell Tensor
+// Cores" compute (Out = A @ B.T, K accumulated slice by slice into a fresh
+// fp32 accumulator).  The data path is the same in spirit -- operand tiles
+// staged in shared memory, moved into per-lane register fragments, multiplied
+// by wavefront-collective matrix instructions -- laid out for CDNA4:
+//
+//   global -> LDS   direct loads (buffer_load_dwordx4 ... lds): each lane
+//                   moves one 16-byte chunk (8 fp16 of one row) straight into
+//                   LDS; a wavefront fills 1 KiB of whole rows per load.
+//   LDS layout      a K slice of a row is BK = 32 or 64 fp16, i.e. 64 or 128
+//                   bytes = 4 or 8 chunks, placed by the XOR swizzles of
+//                   layout.hpp (conflict-free for the direct loads and for
+//                   the fragment reads below).  With BK = 64 the 8 lanes of a
+//                   row fetch one whole 128-byte line, which halves the L2
+//                   requests of BK = 32 (two half-line requests per line).
+//   LDS -> VGPR     one ds_read_b128 per lane per operand fragment: the 8
+//                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 takes
+//                   from each lane.  Both operands are K-contiguous (NT), so
+//                   no transpose is needed.
+//   MFMA            A's fragment is the instruction's first operand, B's
+//                   the second, so in each accumulator register the 32
+//                   lanes of a half-wavefront hold 32 consecutive columns of
+//                   one output row: a dword store per register writes two
+//                   whole 128-byte row segments.
+//   K loop          a ring of LDS stages; each slice's loads are issued
+//                   STAGES-1 slices ahead, spread between MFMAs, and the
+//                   fragments of the next K step are read while the current
+//                   one multiplies; one workgroup barrier per slice.
+//   scheduler       XCD-contiguous ranges of tile ids, grouped so that the
+//                   tiles an XCD runs together share A and B panels in L2.
+//   edges           rows past M or N are clamped on load (their results are
+//                   never stored); K past the end is zero-filled; the
+//                   epilogue masks columns past N and rows past M.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace fp16mc {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Operand element types.  Both move through the kernels as raw 16-bit
+// patterns; only the matrix instruction that consumes them differs.
+struct InF16 {
+  typedef f16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+struct InBF16 {
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// One output element: the fp32 sum, plus the element's previous value when
+// accumulating, stored as fp32 or rounded to nearest-even fp16 / bf16.
+template <class OutT, bool ACC>
+__device__ __forceinline__ void store_out(OutT* p, float v) {
+  if constexpr (ACC) v += static_cast<float>(*p);
+  *p = static_cast<OutT>(v);
+}
+
+// BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
+// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
+// of BK (32 or 64) held in a ring of STAGES LDS stages; WAVES_PER_SIMD
+// workgroups' worth of wavefronts share each SIMD (the register budget
+// follows from it).
+template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_, int BK_ = 32>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
+  static constexpr int BK = BK_;
+  using Swz = LdsSwizzle<2 * BK_>;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int SI = WTM / 32, SJ = WTN / 32;
+  static constexpr int A_STAGE = BM * Swz::kRowBytes;
+  static constexpr int B_STAGE = BN * Swz::kRowBytes;
+  static constexpr int ROWS_PER_WAVE = 1024 / Swz::kRowBytes;     // one 1 KiB direct load
+  static constexpr int ROWS_PER_PASS = (NT / 64) * ROWS_PER_WAVE;
+  static constexpr int A_LOADS = BM / ROWS_PER_PASS;
+  static constexpr int B_LOADS = BN / ROWS_PER_PASS;
+  static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+  static_assert(BK == 32 || BK == 64, "an LDS row holds one 32- or 64-wide K slice");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "rows must split evenly");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static constexpr int WGS_PER_CU = WAVES_PER_SIMD * 256 / NT > 0 ? WAVES_PER_SIMD * 256 / NT : 1;
+  static_assert(LDS_BYTES * WGS_PER_CU <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
+};
+
+using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
+// 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
+// by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
+using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
+// 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
+// 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
+using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64>;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+// Elements [k, k+8) of a row, zero past K.  `row` points at element 0.
+// Only the last, partial K slice of a problem takes this path.
+__device__ __forceinline__ u32x4 load_chunk_masked(const unsigned short* row, int64_t k, int64_t K) {
+  const unsigned short* r16 = row;
+  unsigned int w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (k + e < K) w[e >> 1] |= static_cast<unsigned int>(r16[k + e]) << (16 * (e & 1));
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at lds_span + 16 l; `lds_span` and `soff` are uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned char* lds_span, unsigned voff,
+                                      unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_span, 16, voff, soff, 0, 0);
+}
+
+// 8 consecutive-K values of one M for an MFMA operand from a transposed
+// (MN-contiguous) LDS tile: two ds_read_b64_tr_b16, K rows k..k+3 at `lo` and
+// k+4..k+7 at `hi` (addresses as set up by the kernel).
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+template <class V8>
+__device__ __forceinline__ V8 tr_read8(const unsigned char* lo, const unsigned char* hi) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(lo));
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(hi));
+  return __builtin_bit_cast(V8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Buffer descriptor over [base, base + bytes).  Both values are workgroup-
+// uniform; passing them through readfirstlane lets the compiler keep the
+// descriptor in SGPRs instead of re-checking uniformity at every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// Scheduling hints: keep `n` instructions of one kind together at this point.
+#define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
+#define SCHED_VMEM_READ(n) __builtin_amdgcn_sched_group_barrier(0x020, (n), 0)
+#define SCHED_DS_READ(n) __builtin_amdgcn_sched_group_barrier(0x100, (n), 0)
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// How many of `total` instructions go after the n-th of k MFMAs for an even spread.
+constexpr int spread(int n, int total, int k) { return (n + 1) * total / k - n * total / k; }
+
+// s_waitcnt immediate for "vmcnt(n)" with the other counters left alone (gfx9 encoding).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <class C, class In, class OutT, bool ACC, bool A_MN, bool B_MN>
+__global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD)
+gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B, OutT* __restrict__ Out,
+               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
+               int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m, int64_t tiles_n, int64_t total) {
+  // One array per (operand, stage): the compiler then knows that the
+  // asynchronous LDS writes into one stage never alias reads of another.
+  constexpr int kS = C::STAGES;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a1[C::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a2[kS > 2 ? C::A_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a3[kS > 3 ? C::A_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[C::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b2[kS > 2 ? C::B_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b3[kS > 3 ? C::B_STAGE : 16];
+  auto stage_a = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value % kS;
+    return S == 0 ? lds_a0 : S == 1 ? lds_a1 : S == 2 ? lds_a2 : lds_a3;
+  };
+  auto stage_b = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value % kS;
+    return S == 0 ? lds_b0 : S == 1 ? lds_b1 : S == 2 ? lds_b2 : lds_b3;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
+
+  // ---- tile scheduler -------------------------------------------------------
+  const uint32_t lin = sched::xcd_remap(blockIdx.x, static_cast<uint32_t>(total));
+  const uint32_t per_problem = static_cast<uint32_t>(tiles_m * tiles_n);
+  const uint32_t b = lin / per_problem;
+  const sched::Tile tile = sched::grouped_tile(lin - b * per_problem, static_cast<uint32_t>(tiles_m),
+                                               static_cast<uint32_t>(tiles_n), C::GROUP_M);
+  const int64_t i0 = static_cast<int64_t>(tile.m) * C::BM;
+  const int64_t j0 = static_cast<int64_t>(tile.n) * C::BN;
+  A += b * sA;
+  B += b * sB;
+  Out += b * sO;
+
+  // ---- global -> LDS assignment ------------------------------------------------
+  // Direct load p of wavefront w fills the 1 KiB LDS span [(p*NW + w) KiB,
+  // +1 KiB) of a stage; lane l lands at byte 16 l of it.
+  //   K-contiguous operand (A[i*lda + k]): the span holds RW whole tile rows of
+  //     BK values; lane l fetches the logical chunk that the row swizzle puts
+  //     at its physical slot.  Rows past the matrix edge re-read its last row
+  //     (their results are never stored).  Byte offsets are relative to a
+  //     buffer at the tile's first row: a per-lane offset plus a uniform K
+  //     offset; the last, partial K slice goes through registers with masks.
+  //   MN-contiguous operand (A[k*lda + i]): the span holds 1024/(2W) K rows of
+  //     the tile's W values, placed by the transposed-tile swizzle.  The buffer
+  //     is rebuilt for every slice at the slice's first K row and ends at the
+  //     last element of row K-1, so K rows past the end read as zeros (the
+  //     partial slice needs no special path).  Columns past M read whatever
+  //     memory holds there; they only feed output rows that are never stored.
+  constexpr int NW = C::NT / 64;                   // wavefronts per workgroup
+  constexpr int RW = C::ROWS_PER_WAVE;
+  auto span = [&](int p) { return (p * NW + wave) * 1024; };
+  const int64_t a_ext = (M - i0) < C::BM ? (M - i0) : C::BM;   // valid tile rows (K-contiguous)
+  const int64_t b_ext = (N - j0) < C::BN ? (N - j0) : C::BN;
+  const unsigned short* a_tile = A_MN ? A + i0 : A + i0 * lda;
+  const unsigned short* b_tile = B_MN ? B + j0 : B + j0 * ldb;
+  unsigned a_off[C::A_LOADS];
+  unsigned b_off[C::B_LOADS];
+  // Per-lane byte offsets of the direct loads of one operand.
+  auto setup_offsets = [&](auto mn, auto w, int64_t ext, int64_t ld, unsigned* off, auto loads) {
+    constexpr int kLoadsOp = decltype(loads)::value;
+    if constexpr (!decltype(mn)::value) {
+      const int prow = lane / C::Swz::kChunks;
+      const int pchunk = lane % C::Swz::kChunks;
+#pragma unroll
+      for (int p = 0; p < kLoadsOp; ++p) {
+        const int r = p * C::ROWS_PER_PASS + RW * wave + prow;
+        const int64_t rr = r < ext ? r : ext - 1;
+        off[p] = static_cast<unsigned>(2 * (rr * ld + 8 * C::Swz::logical_chunk(r, pchunk)));
+      }
+    } else {
+      using TZ = TrSwizzle<2 * decltype(w)::value>;
+      constexpr int RK = 1024 / TZ::kRowBytes;     // K rows per 1 KiB span
+      const int kr = lane / TZ::kChunks;
+      const int pc = lane % TZ::kChunks;
+#pragma unroll
+      for (int p = 0; p < kLoadsOp; ++p) {
+        const int k = (p * NW + wave) * RK + kr;
+        off[p] = static_cast<unsigned>(2 * (k * ld + 8 * TZ::logical_chunk(k, pc)));
+      }
+    }
+  };
+  setup_offsets(std::integral_constant<bool, A_MN>{}, std::integral_constant<int, C::BM>{}, a_ext, lda, a_off,
+                std::integral_constant<int, C::A_LOADS>{});
+  setup_offsets(std::integral_constant<bool, B_MN>{}, std::integral_constant<int, C::BN>{}, b_ext, ldb, b_off,
+                std::integral_constant<int, C::B_LOADS>{});
+  // K-contiguous operands: one buffer over the tile's rows for the whole loop.
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_tile, static_cast<unsigned>(2 * ((a_ext - 1) * lda + K)));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_tile, static_cast<unsigned>(2 * ((b_ext - 1) * ldb + K)));
+  // MN-contiguous operands: the buffer of slice `slice` (rows [slice*BK, K)).
+  // The range check works per dword, so the last row's extent is rounded up
+  // to the 16-byte block that holds its last element (same page, never a
+  // fault; the extra values only feed outputs past M or N); rows past the
+  // slice's end still start beyond the range, because ld is a multiple of 8.
+  auto slice_rsrc = [&](const unsigned short* tile, int64_t ld, int64_t cols, int64_t slice) {
+    const int64_t k0 = slice * C::BK;
+    const int64_t rows = (K - k0) < C::BK ? (K - k0) : C::BK;
+    const int64_t last = (2 * cols + 15) & ~int64_t(15);
+    return make_rsrc(tile + k0 * ld, static_cast<unsigned>(2 * (rows - 1) * ld + last));
+  };
+  constexpr int kLoads = C::A_LOADS + C::B_LOADS;   // direct loads per slice per wavefront
+  // All direct loads of slice `slice` (A's, then B's).
+  auto dma_all = [&](unsigned char* as, unsigned char* bs, int64_t slice) {
+    const unsigned koff = static_cast<unsigned>(2 * C::BK * slice);
+    if constexpr (!A_MN) {
+#pragma unroll
+      for (int q = 0; q < C::A_LOADS; ++q) dma16(a_rsrc, as + span(q), a_off[q], koff);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = slice_rsrc(a_tile, lda, M - i0, slice);
+#pragma unroll
+      for (int q = 0; q < C::A_LOADS; ++q) dma16(r, as + span(q), a_off[q], 0);
+    }
+    if constexpr (!B_MN) {
+#pragma unroll
+      for (int q = 0; q < C::B_LOADS; ++q) dma16(b_rsrc, bs + span(q), b_off[q], koff);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = slice_rsrc(b_tile, ldb, N - j0, slice);
+#pragma unroll
+      for (int q = 0; q < C::B_LOADS; ++q) dma16(r, bs + span(q), b_off[q], 0);
+    }
+  };
+  // Last, partial K slice (index nfull): K-contiguous operands through
+  // registers with per-element masks, MN-contiguous ones by direct loads.
+  auto load_tail = [&](unsigned char* as, unsigned char* bs, int64_t slice) {
+    const int64_t k0 = slice * C::BK;
+    if constexpr (!A_MN) {
+#pragma unroll
+      for (int p = 0; p < C::A_LOADS; ++p) {
+        const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + lane / C::Swz::kChunks,
+                                             lane % C::Swz::kChunks);
+        const unsigned short* row = a_tile + a_off[p] / 2 - 8 * lc;
+        *reinterpret_cast<u32x4*>(as + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t r = slice_rsrc(a_tile, lda, M - i0, slice);
+#pragma unroll
+      for (int p = 0; p < C::A_LOADS; ++p) dma16(r, as + span(p), a_off[p], 0);
+    }
+    if constexpr (!B_MN) {
+#pragma unroll
+      for (int p = 0; p < C::B_LOADS; ++p) {
+        const int lc = C::Swz::logical_chunk(p * C::ROWS_PER_PASS + RW * wave + lane / C::Swz::kChunks,
+                                             lane % C::Swz::kChunks);
+        const unsigned short* row = b_tile + b_off[p] / 2 - 8 * lc;
+        *reinterpret_cast<u32x4*>(bs + span(p) + 16 * lane) = load_chunk_masked(row, k0 + 8 * lc, K);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t r = slice_rsrc(b_tile, ldb, N - j0, slice);
+#pragma unroll
+      for (int p = 0; p < C::B_LOADS; ++p) dma16(r, bs + span(p), b_off[p], 0);
+    }
+  };
+
+  // ---- fragment reads + MFMA ------------------------------------------------
+  f32x16 acc[C::SI][C::SJ];
+#pragma unroll
+  for (int si = 0; si < C::SI; ++si)
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj) acc[si][sj] = f32x16{};
+
+  const int frow = mfma32::operand_row(lane);      // row inside a 32-row MFMA tile
+  const int khalf = lane >> 5;                     // which 8-wide K group of a 16-K step
+  const int key = C::Swz::key(frow);          // equal to key(row) for every fragment row
+  const int a_row0 = (wm * C::WTM + frow) * C::Swz::kRowBytes;
+  const int b_row0 = (wn * C::WTN + frow) * C::Swz::kRowBytes;
+  constexpr int KK = C::BK / mfma32::kK;           // 16-wide K steps per slice (2 or 4)
+  constexpr int NMF = C::SI * C::SJ;               // MFMAs per K step
+  // LDS reads per K step: one ds_read_b128 per K-contiguous fragment, two
+  // ds_read_b64_tr_b16 per MN-contiguous one.
+  constexpr int kFr = C::SI * (A_MN ? 2 : 1) + C::SJ * (B_MN ? 2 : 1);
+  static_assert(KK % 2 == 0, "fragments alternate between two register sets");
+
+  struct Frags {
+    typename In::V8 a[C::SI];
+    typename In::V8 b[C::SJ];
+  };
+  // MN-contiguous tiles: lane l = 16g + 4r + q reads K row 8(l/32) + r (+4 for
+  // the second half, +16 kk) at m = 16(g%2) + 4q of each 32-wide MFMA tile;
+  // the swizzle key is a per-lane constant (it uses K-row bits 0, 1 and 3).
+  int a_tr[C::SI];
+  int b_tr[C::SJ];
+  if constexpr (A_MN) {
+    using TZ = TrSwizzle<2 * C::BM>;
+    const int kr = 8 * khalf + ((lane >> 2) & 3);
+    const int mo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int si = 0; si < C::SI; ++si) a_tr[si] = TZ::offset_bytes(kr, wm * C::WTM + 32 * si + mo);
+  }
+  if constexpr (B_MN) {
+    using TZ = TrSwizzle<2 * C::BN>;
+    const int kr = 8 * khalf + ((lane >> 2) & 3);
+    const int mo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj) b_tr[sj] = TZ::offset_bytes(kr, wn * C::WTN + 32 * sj + mo);
+  }
+  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) {
+    const int pc = ((2 * kk + khalf) ^ key) << 4;
+#pragma unroll
+    for (int si = 0; si < C::SI; ++si) {
+      if constexpr (!A_MN) {
+        f.a[si] = *reinterpret_cast<const typename In::V8*>(as + a_row0 + si * 32 * C::Swz::kRowBytes + pc);
+      } else {
+        const unsigned char* p = as + a_tr[si] + 16 * kk * (2 * C::BM);
+        f.a[si] = tr_read8<typename In::V8>(p, p + 4 * (2 * C::BM));
+      }
+    }
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj) {
+      if constexpr (!B_MN) {
+        f.b[sj] = *reinterpret_cast<const typename In::V8*>(bs + b_row0 + sj * 32 * C::Swz::kRowBytes + pc);
+      } else {
+        const unsigned char* p = bs + b_tr[sj] + 16 * kk * (2 * C::BN);
+        f.b[sj] = tr_read8<typename In::V8>(p, p + 4 * (2 * C::BN));
+      }
+    }
+  };
+  auto mfma = [&](const Frags& f, int n) {
+    const int si = n / C::SJ, sj = n % C::SJ;
+    acc[si][sj] = In::mfma32(f.a[si], f.b[sj], acc[si][sj]);
+  };
+  auto mfma_all = [&](const Frags& f) {
+#pragma unroll
+    for (int n = 0; n < NMF; ++n) mfma(f, n);
+  };
+  // Wait until at most `n` direct loads of this thread are in flight and its
+  // LDS reads/writes are done, then make everyone's writes visible.
+  // (A plain s_barrier: a fenced __syncthreads would also wait for the loads
+  // that are meant to stay in flight.)
+  auto publish_keep = [&](auto n) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(n)::value) & ~(15 << 8));  // lgkmcnt(0) as well
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // ---- K loop --------------------------------------------------------------------
+  // Full slice s lives in stage s % S of an S-stage ring.  Slices s+1 ..
+  // s+S-2 are already in flight when phase s begins; phase s issues slice
+  // s+S-1 into the stage of slice s-1, whose reads all completed before the
+  // barrier that opened the phase.  In phase s a wavefront
+  //   1. reads the fragments of K step (s, 0);
+  //   2. issues the MFMAs of step (s-1, KK-1), read before the barrier;
+  //   3. for kk = 1 .. KK-1 issues the MFMAs of step (s, kk-1) with the
+  //      fragment reads of step (s, kk) spread between them;
+  //   4. waits until slice s+1 has landed (only the S-2 later slices may
+  //      still be in flight) and its own fragment reads are done; barrier.
+  // Slice s+S-1's loads are spread over the MFMAs of the first two steps of
+  // 2 and 3, so that they leave early in the phase.  The MFMA pipe restarts
+  // after each barrier on registers that are already loaded.
+  constexpr int kAhead = kS - 1;                   // prefetch distance in slices
+  const int64_t nfull = K / C::BK;
+  Frags f0, f1;
+  auto slice_of = [&](int64_t slice) {
+    // slices past the end reload the last one into an idle stage: no branch, never read
+    return slice < nfull ? slice : nfull - 1;
+  };
+  std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
+  constexpr int kLoadSteps = 2;                    // MFMA steps the slice loads are spread over
+  auto phase = [&](auto st, int64_t s, auto pending) {
+    constexpr int S = decltype(st)::value;
+    constexpr bool kPending = decltype(pending)::value;
+    unsigned char* as = stage_a(st);
+    unsigned char* bs = stage_b(st);
+    unsigned char* an = stage_a(std::integral_constant<int, S + kAhead>{});
+    unsigned char* bn = stage_b(std::integral_constant<int, S + kAhead>{});
+    const int64_t next = slice_of(s + kAhead);
+    read_frags(as, bs, 0, f0);
+    if constexpr (kPending) mfma_all(f1);
+    dma_all(an, bn, next);
+    static_for<KK - 1>([&](auto t) {
+      constexpr int kk = decltype(t)::value + 1;
+      if constexpr (kk % 2 == 1) {
+        read_frags(as, bs, kk, f1);
+        mfma_all(f0);
+      } else {
+        read_frags(as, bs, kk, f0);
+        mfma_all(f1);
+      }
+    });
+    // Issue order for the scheduler: each step's fragment reads spread between
+    // the previous step's MFMAs, the slice loads between the first two steps'.
+    SCHED_DS_READ(kFr);
+    constexpr int v0 = spread(0, kLoads, kLoadSteps);
+    if constexpr (kPending) {
+      static_for<NMF>([&](auto n) {
+        constexpr int v = spread(decltype(n)::value, v0, NMF);
+        SCHED_MFMA(1);
+        if constexpr (v > 0) SCHED_VMEM_READ(v);
+      });
+    } else {
+      SCHED_VMEM_READ(v0);
+    }
+    static_for<KK - 1>([&](auto t) {
+      constexpr int g = decltype(t)::value + 1;
+      constexpr int vg = g < kLoadSteps ? spread(g, kLoads, kLoadSteps) : 0;
+      static_for<NMF>([&](auto n) {
+        constexpr int d = spread(decltype(n)::value, kFr, NMF);
+        constexpr int v = spread(decltype(n)::value, vg, NMF);
+        SCHED_MFMA(1);
+        if constexpr (d > 0) SCHED_DS_READ(d);
+        if constexpr (v > 0) SCHED_VMEM_READ(v);
+      });
+    });
+    publish_keep(keep_later);
+  };
+  std::integral_constant<bool, true> with_pending;
+  std::integral_constant<bool, false> first;
+  if (nfull > 0 && nfull <= kAhead) {
+    // Short K: every full slice fits in the ring at once -- load them all,
+    // one barrier, multiply.
+    static_for<kAhead>([&](auto i) {
+      if (decltype(i)::value < nfull) dma_all(stage_a(i), stage_b(i), decltype(i)::value);
+    });
+    publish_keep(std::integral_constant<int, 0>{});
+    static_for<kAhead>([&](auto i) {
+      if (decltype(i)::value < nfull) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          read_frags(stage_a(i), stage_b(i), kk, f0);
+          mfma_all(f0);
+        }
+      }
+    });
+  } else if (nfull > 0) {
+    static_for<kAhead>([&](auto i) { dma_all(stage_a(i), stage_b(i), slice_of(decltype(i)::value)); });
+    publish_keep(keep_later);
+    phase(std::integral_constant<int, 0>{}, 0, first);
+    int64_t s = 1;
+    for (; s + kS <= nfull; s += kS) {
+      static_for<kS>([&](auto i) {
+        phase(std::integral_constant<int, (decltype(i)::value + 1) % kS>{}, s + decltype(i)::value, with_pending);
+      });
+    }
+    static_for<kS - 1>([&](auto i) {
+      if (s < nfull) {
+        phase(std::integral_constant<int, (decltype(i)::value + 1) % kS>{}, s, with_pending);
+        ++s;
+      }
+    });
+    mfma_all(f1);  // step (nfull-1, KK-1)
+    // drain the idle reloads before any stage is reused or the workgroup ends
+    publish_keep(std::integral_constant<int, 0>{});
+  }
+  // The partial slice, if any, goes through registers into stage nfull % S
+  // (unused by the short path, idle after the pipelined one).
+  if (K % C::BK != 0) {
+    const int st = static_cast<int>(nfull % kS);
+    unsigned char* as = lds_a0;
+    unsigned char* bs = lds_b0;
+    static_for<kS>([&](auto i) {
+      if (st == decltype(i)::value) {
+        as = stage_a(i);
+        bs = stage_b(i);
+      }
+    });
+    load_tail(as, bs, nfull);
+    publish_keep(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      read_frags(as, bs, kk, f0);
+      mfma_all(f0);
+    }
+  }
+
+  // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
+  // i = i0 + wm*WTM + 32 si + 8(v/4) + 4(l/32) + v%4, j = j0 + wn*WTN + 32 sj + l%32:
+  // one dword store per v writes two whole 128-byte row segments.  When
+  // accumulating, a row block's previous values are all loaded before any of
+  // its stores (ldo is a run-time value, so the compiler cannot prove that a
+  // store does not alias a later load and would otherwise wait on each load).
+#pragma unroll
+  for (int si = 0; si < C::SI; ++si) {
+    float prev[C::SJ][16];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int sj = 0; sj < C::SJ; ++sj) {
+        const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+          prev[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj) {
+      const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+        const float val = ACC ? acc[si][sj][v] + prev[sj][v] : acc[si][sj][v];
+        if (i < M && j < N) Out[i * ldo + j] = static_cast<OutT>(val);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny products (N <= 16): Out (M x N) = A (M x K) @ B (N x K)^T.
+// The work is a stream over A (each element used once), so A bypasses LDS:
+// every lane loads four 16-byte chunks of one row per 128-wide K block (the
+// four lanes of a row cover its 256 bytes), and B -- padded with zero
+// columns to 16 -- is loaded in the same K order, which is all the MFMA
+// needs (any K order gives the same sum as long as both operands agree).
+// v_mfma_f32_16x16x32_f16: lane l supplies row/column l%16 and 8 fp16 of K;
+// here lane (r = l%16, q = l/16) of MFMA step j uses K elements
+// kb + 32j + 8q .. +8 of its row, so each load instruction covers 64
+// contiguous bytes of 16 rows (a quarter-line per lane scattered over 256
+// bytes measured 29% slower).  The last, partial block uses K elements
+// kb + 32q + 8j instead (any order works while A and B agree).  Eight
+// wavefronts split K; their partial 64 x 16 results are summed through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kSkRows = 64;        // output rows per workgroup (4 MFMA row tiles)
+constexpr int kSkWaves = 8;        // wavefronts splitting K
+constexpr int kSkBlock = 128;      // K per block per wavefront
+
+// Four 16-byte chunks of a row at elements k + 32 j (all inside K).  With
+// k = kb + 8q the four lanes of a row read 64 contiguous bytes per load.
+__device__ __forceinline__ void sk_load(const unsigned short* row, int64_t k, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const u32x4*>(row + k + 32 * j);
+}
+// The same with zeros past K (the last, partial block only).
+__device__ __forceinline__ void sk_load_masked(const unsigned short* row, int64_t k, int64_t K, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = load_chunk_masked(row, k + 8 * j, K);
+}
+
+template <class In, class OutT, bool ACC>
+__global__ void __launch_bounds__(kSkWaves * 64, 1)
+gemm_nt_skinny_kernel(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B,
+                      OutT* __restrict__ Out,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
+                      int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m) {
+  __shared__ float red[kSkWaves][kSkRows][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t b = blockIdx.x / static_cast<uint32_t>(tiles_m);
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x - b * static_cast<uint32_t>(tiles_m)) * kSkRows;
+  A += b * sA;
+  B += b * sB;
+  Out += b * sO;
+
+  const int r = mfma16::operand_row(lane);   // row in a 16-row tile / column of B
+  const int q = lane >> 4;                   // 32-element quarter of the block
+  const unsigned short* arow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t i = i0 + 16 * t + r;
+    arow[t] = A + (i < M ? i : M - 1) * lda;
+  }
+  // lanes past N read row N-1 (in bounds) and zero it: no divergent branch
+  const bool has_b = r < N;
+  const unsigned short* brow = B + (has_b ? r : N - 1) * ldb;
+  const unsigned bmask = has_b ? 0xFFFFFFFFu : 0u;
+
+  // Full 128-wide K blocks are split evenly over the wavefronts; the last,
+  // partial block (if any) goes to the last wavefront with masked loads.
+  const int64_t nfull = K / kSkBlock;
+  const int64_t per = (nfull + kSkWaves - 1) / kSkWaves;
+  const int64_t blk0 = wave * per < nfull ? wave * per : nfull;
+  const int64_t blk1 = (blk0 + per < nfull) ? blk0 + per : nfull;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{};
+  u32x4 va[2][4][4];
+  u32x4 vb[2][4];
+  auto load = [&](int buf, int64_t blk) {
+    const int64_t k = blk * kSkBlock + 8 * q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sk_load(arow[t], k, va[buf][t]);
+    sk_load(brow, k, vb[buf]);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const typename In::V8 bj = __builtin_bit_cast(typename In::V8, vb[buf][j] & bmask);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = In::mfma16(__builtin_bit_cast(typename In::V8, va[buf][t][j]), bj, acc[t]);
+    }
+  };
+  if (blk0 < blk1) {
+    load(0, blk0);
+    int64_t blk = blk0;
+    for (; blk + 2 < blk1; blk += 2) {  // blocks blk+1 and blk+2 exist: no branch in the body
+      load(1, blk + 1);
+      mma(0);
+      load(0, blk + 2);
+      mma(1);
+    }
+    if (blk + 1 < blk1) {
+      load(1, blk + 1);
+      mma(0);
+      mma(1);
+    } else {
+      mma(0);
+    }
+  }
+  if (K % kSkBlock != 0 && wave == kSkWaves - 1) {
+    const int64_t k = nfull * kSkBlock + 32 * q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sk_load_masked(arow[t], k, K, va[0][t]);
+    sk_load_masked(brow, k, K, vb[0]);
+    mma(0);
+  }
+
+  // partial sums -> LDS: element v of lane l in row tile t is (row 16t + 4(l/16) + v, column l%16)
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][16 * t + mfma16::acc_row(lane, v)][mfma16::acc_col(lane, v)] = acc[t][v];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kSkRows * 16; e += kSkWaves * 64) {
+    const int row = e / 16, col = e % 16;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) sum += red[w][row][col];
+    const int64_t i = i0 + row;
+    if (i < M && col < N) store_out<OutT, ACC>(Out + i * ldo + col, sum);
+  }
+}
+
+template <class C>
+int64_t tiles_of(int64_t M, int64_t N, int64_t batch, int64_t* tm, int64_t* tn) {
+  *tm = (M + C::BM - 1) / C::BM;
+  *tn = (N + C::BN - 1) / C::BN;
+  return *tm * *tn * batch;
+}
+
+template <class C, class In, class OutT, bool ACC, bool A_MN, bool B_MN>
+hipError_t launch(const GemmProblem& p, hipStream_t stream) {
+  int64_t tm, tn;
+  const int64_t total = tiles_of<C>(p.M, p.N, p.batch, &tm, &tn);
+  const unsigned short* A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* B = static_cast<const unsigned short*>(p.B);
+  OutT* Out = static_cast<OutT*>(p.Out);
+  int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
+  int64_t sA = p.sA, sB = p.sB, sO = p.sO;
+  void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tm, &tn,
+                  const_cast<int64_t*>(&total)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_kernel<C, In, OutT, ACC, A_MN, B_MN>),
+                         dim3(static_cast<unsigned>(total)), dim3(C::NT), args, 0, stream);
+}
+
+template <class In, class OutT, bool ACC>
+hipError_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
+  const unsigned short* A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* B = static_cast<const unsigned short*>(p.B);
+  OutT* Out = static_cast<OutT*>(p.Out);
+  int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
+  int64_t sA = p.sA, sB = p.sB, sO = p.sO;
+  int64_t tiles_m = (M + kSkRows - 1) / kSkRows;
+  void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tiles_m};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_skinny_kernel<In, OutT, ACC>),
+                         dim3(static_cast<unsigned>(tiles_m * p.batch)), dim3(kSkWaves * 64), args, 0, stream);
+}
+
+template <class T>
+struct Tag {
+  typedef T type;
+};
+
+// Calls f(Tag<In>, Tag<OutT>, integral_constant<bool, ACC>) for the problem's types.
+template <class F>
+hipError_t with_types(const GemmProblem& p, F&& f) {
+  std::integral_constant<bool, true> acc;
+  std::integral_constant<bool, false> fresh;
+  if (p.ab_type == Dtype::kBF16) {
+    if (p.out_type == Dtype::kF32) return p.accumulate ? f(Tag<InBF16>{}, Tag<float>{}, acc) : f(Tag<InBF16>{}, Tag<float>{}, fresh);
+    return p.accumulate ? f(Tag<InBF16>{}, Tag<__bf16>{}, acc) : f(Tag<InBF16>{}, Tag<__bf16>{}, fresh);
+  }
+  if (p.out_type == Dtype::kF32) return p.accumulate ? f(Tag<InF16>{}, Tag<float>{}, acc) : f(Tag<InF16>{}, Tag<float>{}, fresh);
+  return p.accumulate ? f(Tag<InF16>{}, Tag<_Float16>{}, acc) : f(Tag<InF16>{}, Tag<_Float16>{}, fresh);
+}
+
+template <class C, bool A_MN, bool B_MN>
+hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
+  return with_types(p, [&](auto in, auto out, auto acc) {
+    return launch<C, typename decltype(in)::type, typename decltype(out)::type, decltype(acc)::value, A_MN, B_MN>(
+        p, stream);
+  });
+}
+
+hipError_t launch_skinny_typed(const GemmProblem& p, hipStream_t stream) {
+  return with_types(p, [&](auto in, auto out, auto acc) {
+    return launch_skinny<typename decltype(in)::type, typename decltype(out)::type, decltype(acc)::value>(p, stream);
+  });
+}
+
+template <class C>
+int64_t plan_tiles(int64_t M, int64_t N, int64_t batch) {
+  int64_t tm, tn;
+  return tiles_of<C>(M, N, batch, &tm, &tn);
+}
+
+// Launch of one plan for one storage order of the operands.
+template <bool A_MN, bool B_MN>
+hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream) {
+  switch (plan) {
+    case GemmPlan::kWave32: return launch_cfg<CfgWave32, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x64: return launch_cfg<CfgWg128x64, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256: return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
+    case GemmPlan::kSkinny:
+      if constexpr (!A_MN && !B_MN) return launch_skinny_typed(p, stream);
+      return hipErrorInvalidValue;   // the plan logic never picks it for transposed operands
+    default: return hipSuccess;
+  }
+}
+
+}  // namespace
+}  // namespace fp16mc

@@ -9,9 +9,11 @@ namespace fp16mc {
 // Element types; the values equal fp16mc_dtype of the C header.
 enum class Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// One batched NT product: problem b reads A + b*sA, B + b*sB, writes Out + b*sO
+// One batched product: problem b reads A + b*sA, B + b*sB, writes Out + b*sO
 // (strides in elements).  A and B hold ab_type (F16 or BF16); Out holds
 // out_type (F32 or ab_type); with `accumulate` Out's previous values are added.
+// a_mn / b_mn: the operand is stored with K indexing its rows (A[k*lda + i],
+// B[k*ldb + j]) instead of K-contiguous rows (A[i*lda + k], B[j*ldb + k]).
 struct GemmProblem {
   const void* A;
   const void* B;
@@ -23,6 +25,8 @@ struct GemmProblem {
   Dtype ab_type;
   Dtype out_type;
   bool accumulate;
+  bool a_mn;
+  bool b_mn;
 };
 
 // Kernel configurations, one per shape class.
@@ -34,14 +38,19 @@ enum class GemmPlan : int {
   kSkinny = 4,    // N <= 16: 8 wavefronts split K over 64 rows, A streamed past LDS
 };
 
-GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch);
+GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool a_mn, bool b_mn);
 const char* gemm_plan_name(GemmPlan plan);
 // Number of workgroups the plan launches (host-side; used to validate the grid).
 int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch);
 hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+// One storage order each (gemm_nt.hip, gemm_nn.hip, gemm_tt.hip, gemm_tn.hip).
+hipError_t launch_gemm_nt(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_nn(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_tt(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_tn(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
 // True when every operand tile of the plan spans fewer than 2^32 bytes (the
 // kernels address a tile through a buffer descriptor with 32-bit offsets).
-bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb);
+bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, bool a_mn, bool b_mn);
 
 // Fragment copy; `groups` = num_tiles / num.
 hipError_t launch_frag_copy(const void* src, void* dst, int64_t groups, int num, bool col_major,

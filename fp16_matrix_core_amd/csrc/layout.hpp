@@ -67,6 +67,45 @@ struct LdsSwizzle : RowSwizzle<RowBytes> {
 };
 
 // ---------------------------------------------------------------------------
+// Transposed operand tiles.  An operand stored with M (or N) contiguous is
+// staged as it lies in memory: LDS row k holds the tile's RowBytes/2 values
+// of K index k.  A matrix-instruction fragment needs 8 consecutive K of one
+// M, which ds_read_b64_tr_b16 delivers: in each 16-lane group, lane 4r + q
+// names 8 bytes (4 values) of "row" r of a 4 x 16 block and lane i receives
+// column i of that block (measured on gfx950).  Lane l = 16 g + 4 r + q of a
+// fragment read takes LDS row k0 + r with k0 = 8 (l / 32) (+4 for the
+// second half of the 8 K values) and the 4 values at m = 16 (g % 2) + 4 q.
+//
+// Chunk c of row k is stored at physical chunk c ^ key(k), with
+//   64-byte rows    key = 2 ((k >> 3) & 1)
+//   128-byte rows   key = 4 ((k >> 1) & 1) + 2 ((k >> 3) & 1)
+//   >= 256 bytes    key = 4 (k & 3) + 2 ((k >> 3) & 1)   (low 4 chunk bits)
+// so that the 32 lanes served together -- lanes [0, 32) and [32, 64), or
+// lanes with equal bit 4 -- touch 64 distinct banks (tests/host simulates
+// both pairings).  The key uses only bits 0, 1 and 3 of k, i.e. it is a
+// per-lane constant of a fragment read.  Direct loads fill whole rows as
+// contiguous 1 KiB spans, as for K-contiguous tiles.
+// ---------------------------------------------------------------------------
+template <int RowBytes>
+struct TrSwizzle {
+  static_assert(RowBytes == 64 || RowBytes == 128 || (RowBytes >= 256 && RowBytes % 256 == 0),
+                "transposed tiles are 32, 64 or a multiple of 128 values wide");
+  static constexpr int kRowBytes = RowBytes;
+  static constexpr int kChunks = RowBytes / 16;
+  FP16MC_HD static constexpr int key(int k) {
+    return RowBytes == 64    ? 2 * ((k >> 3) & 1)
+           : RowBytes == 128 ? 4 * ((k >> 1) & 1) + 2 * ((k >> 3) & 1)
+                             : 4 * (k & 3) + 2 * ((k >> 3) & 1);
+  }
+  FP16MC_HD static constexpr int phys_chunk(int k, int chunk) { return chunk ^ key(k); }
+  FP16MC_HD static constexpr int logical_chunk(int k, int phys) { return phys ^ key(k); }
+  // byte offset of element m of row k
+  FP16MC_HD static constexpr int offset_bytes(int k, int m) {
+    return k * RowBytes + (phys_chunk(k, m >> 3) << 4) + 2 * (m & 7);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // v_mfma_f32_32x32x16_f16: D(32x32) += X(32x16) * Y(16x32), fp16 in, fp32 acc.
 // Operands: lane l supplies 8 fp16 of X row (l % 32), and 8 fp16 of Y column
 // (l % 32), both at k = 8*(l / 32) + e, e in [0, 8).

@@ -123,6 +123,40 @@ int gemm_nt_ex(const void* A, const void* B, void* Out,
                int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
                int ab_type, int out_type, int accumulate, void* stream);
 
+/* Storage orders of the operands of gemm_ex. */
+enum {
+  FP16MC_K_CONTIGUOUS = 0,  /* rows hold K: A[i*lda + k], B[j*ldb + k]          */
+  FP16MC_MN_CONTIGUOUS = 1  /* rows are K indices: A[k*lda + i], B[k*ldb + j]   */
+};
+
+/*
+ * The general form: gemm_nt_ex with a choice of storage order per operand.
+ *
+ *   Out[i*ldo + j] = round_out( sum_{k<K} a(i,k) * b(j,k)  (+ Out[i*ldo + j]) )
+ *   a(i,k) = A[i*lda + k] (a_order = FP16MC_K_CONTIGUOUS) or A[k*lda + i]
+ *            (FP16MC_MN_CONTIGUOUS: A stored K x M, M contiguous)
+ *   b(j,k) = B[j*ldb + k] (b_order = FP16MC_K_CONTIGUOUS) or B[k*ldb + j]
+ *            (FP16MC_MN_CONTIGUOUS: B stored K x N, N contiguous)
+ *
+ * With both operands K-contiguous this is Out = A @ B.T (gemm_nt_ex); with B
+ * stored K x N it is the plain product Out = A @ B.  An operand stored with M
+ * (or N) contiguous is staged in LDS as it lies in memory and its fragments
+ * are read with the LDS transpose read -- the role of the matrix load's
+ * transposing variant ("Warp Matrix Instructions", "Other Fragment Shapes and
+ * Transfers": the transpose acts on each 8x8 matrix of 16-bit elements; "copy
+ * -> ldstmatrix", column-major shared layouts).
+ *
+ * Preconditions as gemm_nt_ex, except that a K x M operand needs lda >= M
+ * (K x N: ldb >= N) and that an operand stored K x W addresses BK = 64 of its
+ * rows at a time with 32-bit byte offsets: 2*64*ld < 2^32.  a_order and
+ * b_order outside the enum are FP16MC_EINVAL.  Result accuracy as gemm_nt_ex.
+ */
+int gemm_ex(const void* A, const void* B, void* Out,
+            int64_t M, int64_t N, int64_t K,
+            int64_t lda, int64_t ldb, int64_t ldo,
+            int64_t batch, int64_t strideA, int64_t strideB, int64_t strideO,
+            int a_order, int b_order, int ab_type, int out_type, int accumulate, void* stream);
+
 /* Directions of frag_copy. */
 enum {
   FRAG_LOAD = 0,     /* shared image  -> fragment (the ldmatrix direction)  */
@@ -171,6 +205,9 @@ int frag_copy(const void* src, void* dst, int64_t num_tiles, int num,
  * logic, no HIP call.
  */
 const char* gemm_nt_f16f32_plan(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/* The same for gemm_ex with the given storage orders (pure host logic). */
+const char* gemm_ex_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int a_order, int b_order);
 
 /*
  * Message describing the last failed call on this thread ("" if none).  The

@@ -10,9 +10,10 @@ Contents
   gemm   Out = A @ B.T for fp16 A (M,K), B (N,K): the plain definition in
          float64 (products of fp16 values are exact in float64), plus the
          per-element bound sum_k |A[i,k] * B[j,k]| that the parity test scales.
-  gemm_ex  the general product: bfloat16 operands (decoded from their bit
-         patterns), the output's previous values as the MMA's C operand, and
-         the acceptance rule for float16 / bfloat16 outputs.
+  general  the general product: bfloat16 operands (decoded from their bit
+         patterns), operands stored with K indexing their rows, the output's
+         previous values as the MMA's C operand, and the acceptance rule for
+         float16 / bfloat16 outputs.
   frag   the bit-exact model of the warp-collective 8x8 matrix load/store
          (ldmatrix/stmatrix): shared image <-> per-lane register fragment, for
          num in {1, 2, 4} tiles, row- or column-major shared layouts.
@@ -25,7 +26,9 @@ Instructions", "Blackwell Tensor Cores", "copy -> ldstmatrix").
 """
 
 from .gemm import gemm_nt, gemm_nt_loops, gemm_nt_strided, gemm_nt_rows, gemm_nt_batched, within_bound  # noqa: F401
-from .gemm_ex import bf16_to_f64, operand_f64, gemm_nt_ex, half_ulp, within_bound_out  # noqa: F401
+from .general import (  # noqa: F401
+    bf16_to_f64, operand_f64, gemm_nt_ex, gemm_ex, gemm_ex_strided, half_ulp, within_bound_out,
+)
 from .frag import (  # noqa: F401
     register_layout, shared_layout, fit_shared_layout, image_index,
     frag_load, frag_store, frag_roundtrip,

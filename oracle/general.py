@@ -16,6 +16,13 @@ Definitions followed
               bits of an IEEE binary32, so widening it to float64 is exact.
               Products of two bfloat16 values have at most 16 significant bits
               and are exact in float64, as for float16.
+  storage     "Warp Matrix Instructions", "Other Fragment Shapes and
+  order       Transfers": the matrix load has a transposing variant that acts
+              on each 8x8 matrix of 16-bit elements; "copy -> ldstmatrix"
+              accepts row- and column-major shared layouts.  Reading taken: an
+              operand may be stored with K indexing its rows (A as K x M,
+              a(i, k) = A[k*lda + i]; B as K x N, b(j, k) = B[k*ldb + j]); the
+              product is the same sum over the same logical values.
   16-bit out  the pages only produce fp32 results.  Reading taken: a float16
               or bfloat16 output is the fp32 result rounded to nearest even in
               that format (values past its range become +-inf).
@@ -28,7 +35,8 @@ can add.
 
 import numpy as np
 
-__all__ = ["bf16_to_f64", "operand_f64", "gemm_nt_ex", "half_ulp", "within_bound_out"]
+__all__ = ["bf16_to_f64", "operand_f64", "gemm_nt_ex", "gemm_ex", "gemm_ex_strided", "half_ulp",
+           "within_bound_out"]
 
 # significand bits (incl. the implicit one) and minimum normal exponent per format
 _FORMATS = {"f16": (11, -14), "bf16": (8, -126)}
@@ -81,6 +89,41 @@ def gemm_nt_ex(A, B, C=None, ab="f16", c_fmt="f32"):
         ref = ref + c
         bound = bound + np.abs(c)
     return ref, bound
+
+
+def gemm_ex(A, B, C=None, ab="f16", a_order="k", b_order="k", c_fmt="f32"):
+    """Reference and bound for Out = a @ b^T (+ C) with either storage order per operand.
+
+    a_order 'k': A is (M, K), a(i, k) = A[i, k]; 'mn': A is stored (K, M),
+    a(i, k) = A[k, i].  Likewise b_order for B ((N, K) or stored (K, N)).
+    """
+    A = np.asarray(A)
+    B = np.asarray(B)
+    if a_order not in ("k", "mn") or b_order not in ("k", "mn"):
+        raise ValueError("storage orders are 'k' or 'mn'")
+    a = A if a_order == "k" else A.T
+    b = B if b_order == "k" else B.T
+    return gemm_nt_ex(np.ascontiguousarray(a), np.ascontiguousarray(b), C, ab=ab, c_fmt=c_fmt)
+
+
+def gemm_ex_strided(a_flat, b_flat, M, N, K, lda, ldb, ab="f16", a_order="k", b_order="k", C=None):
+    """Oracle seen through the library's buffer view, element by element.
+
+    a(i, k) = a_flat[i*lda + k] ('k') or a_flat[k*lda + i] ('mn'); b(j, k) =
+    b_flat[j*ldb + k] or b_flat[k*ldb + j].  Elements outside these index sets
+    (the padding between rows) are never read.
+    """
+    a_flat = np.asarray(a_flat)
+    b_flat = np.asarray(b_flat)
+    a = np.empty((M, K), dtype=a_flat.dtype)
+    b = np.empty((N, K), dtype=b_flat.dtype)
+    for i in range(M):
+        for k in range(K):
+            a[i, k] = a_flat[i * lda + k] if a_order == "k" else a_flat[k * lda + i]
+    for j in range(N):
+        for k in range(K):
+            b[j, k] = b_flat[j * ldb + k] if b_order == "k" else b_flat[k * ldb + j]
+    return gemm_nt_ex(a, b, C, ab=ab)
 
 
 def half_ulp(x, fmt):

@@ -77,9 +77,98 @@ void check_swizzle() {
   }
 }
 
+// ds_read_b64_tr_b16 as measured on gfx950: in each 16-lane group G, lane
+// 4e + j (e, j < 4) names 8 bytes = row e, columns 4j..4j+3 of a 4 x 16 block;
+// lane i of the group receives column i.  `img` is LDS as b16 values.
+static void tr16_read(const std::vector<int>& img, const int (&addr)[64], int (&out)[64][4]) {
+  for (int L = 0; L < 64; ++L) {
+    const int G = L / 16, i = L % 16;
+    for (int e = 0; e < 4; ++e) out[L][e] = img[(addr[16 * G + 4 * e + i / 4] >> 1) + (i % 4)];
+  }
+}
+
+// 64-bit LDS reads: conflict-free iff each 32-lane pass touches 64 distinct
+// banks; `pairing` 0: passes [0,32) and [32,64); 1: passes by lane bit 4.
+static bool b64_conflict_free(const int (&addr)[64], int pairing) {
+  for (int pass = 0; pass < 2; ++pass) {
+    std::set<int> banks;
+    int n = 0;
+    for (int l = 0; l < 64; ++l) {
+      const int which = pairing == 0 ? (l >> 5) : ((l >> 4) & 1);
+      if (which != pass) continue;
+      for (int d = 0; d < 2; ++d) banks.insert((addr[l] / 4 + d) % 64);
+      n += 2;
+    }
+    if ((int)banks.size() != n) return false;
+  }
+  return true;
+}
+
+// Transposed tiles: bijective rows, whole-row direct loads, fragment reads that
+// deliver the MFMA operand map, conflict-free under both pass pairings.
+template <int RowBytes>
+void check_tr_swizzle(int bk) {
+  using Z = TrSwizzle<RowBytes>;
+  const int W = RowBytes / 2;   // values per row
+  for (int k = 0; k < 64; ++k) {
+    std::set<int> seen;
+    for (int c = 0; c < Z::kChunks; ++c) {
+      seen.insert(Z::phys_chunk(k, c));
+      CHECK(Z::logical_chunk(k, Z::phys_chunk(k, c)) == c, "tr inverse");
+    }
+    CHECK((int)seen.size() == Z::kChunks, "tr swizzle not a bijection (%d-byte rows, k %d)", RowBytes, k);
+  }
+  // direct loads: a 1 KiB span of whole rows, every (row, chunk) once
+  for (int s0 = 0; s0 < bk * RowBytes; s0 += 1024) {
+    std::set<int> offs;
+    for (int l = 0; l < 64; ++l) {
+      const int byte = s0 + 16 * l;
+      const int k = byte / RowBytes, pc = (byte % RowBytes) / 16;
+      offs.insert(Z::offset_bytes(k, 8 * Z::logical_chunk(k, pc)));
+    }
+    CHECK(offs.size() == 64 && *offs.begin() == s0 && *offs.rbegin() == s0 + 63 * 16, "tr direct-load span");
+  }
+  // LDS image of a tile whose value at (k, m) is k * 1000 + m
+  std::vector<int> img(bk * W);
+  for (int k = 0; k < bk; ++k)
+    for (int m = 0; m < W; ++m) img[Z::offset_bytes(k, m) / 2] = k * 1000 + m;
+  for (int kk = 0; kk < bk / 16; ++kk)
+    for (int t = 0; t < 2; ++t)
+      for (int mbase = 0; mbase < W; mbase += 32) {
+        int addr[64];
+        for (int l = 0; l < 64; ++l) {
+          const int r = (l >> 2) & 3, q = l & 3;
+          const int k = 16 * kk + 8 * (l >> 5) + 4 * t + r;
+          addr[l] = Z::offset_bytes(k, mbase + 16 * ((l >> 4) & 1) + 4 * q);
+        }
+        int got[64][4];
+        tr16_read(img, addr, got);
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 4; ++e) {
+            const int k = 16 * kk + mfma32::operand_k(l, 4 * t + e), m = mbase + mfma32::operand_row(l);
+            CHECK(got[l][e] == k * 1000 + m, "tr fragment wrong: rows %d, lane %d, e %d", RowBytes, l, e);
+          }
+        CHECK(b64_conflict_free(addr, 0), "tr read conflicts (pairing 0, %d-byte rows, kk %d t %d m %d)",
+              RowBytes, kk, t, mbase);
+        CHECK(b64_conflict_free(addr, 1), "tr read conflicts (pairing 1, %d-byte rows, kk %d t %d m %d)",
+              RowBytes, kk, t, mbase);
+      }
+  // the swizzle is needed: unswizzled rows conflict under at least one pairing
+  if (RowBytes >= 128) {
+    int addr[64];
+    for (int l = 0; l < 64; ++l)
+      addr[l] = (8 * (l >> 5) + ((l >> 2) & 3)) * RowBytes + 2 * (16 * ((l >> 4) & 1) + 4 * (l & 3));
+    CHECK(!(b64_conflict_free(addr, 0) && b64_conflict_free(addr, 1)), "unswizzled tr rows should conflict");
+  }
+}
+
 int main() {
   check_swizzle<64>();
   check_swizzle<128>();
+  check_tr_swizzle<64>(32);
+  check_tr_swizzle<128>(64);
+  check_tr_swizzle<256>(64);
+  check_tr_swizzle<512>(64);
   // the model reproduces the measured conflicts of unswizzled rows
   {
     int addr[64];

@@ -42,8 +42,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert {"gemm_nt_f16f32", "gemm_nt_f16f32_batched", "gemm_nt_ex", "frag_copy", "fp16mc_last_error",
-            "gemm_nt_f16f32_plan"} <= set(names)
+    assert {"gemm_nt_f16f32", "gemm_nt_f16f32_batched", "gemm_nt_ex", "gemm_ex", "frag_copy",
+            "fp16mc_last_error", "gemm_nt_f16f32_plan", "gemm_ex_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     nm = subprocess.run(["nm", "-D", "--defined-only", fbuild.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
@@ -114,6 +114,35 @@ def test_gemm_ex_output_alignment_follows_the_output_type(L):
     # the old entry points are gemm_nt_ex(F16, F32, fresh): same checks, same codes
     assert L.gemm_nt_ex(*EX_OK[:8], 4, 1, 0, 0, 0, 1, 0, 0, None) == -1
     assert L.gemm_nt_f16f32(*EX_OK[:8], 4, None) == -1
+
+
+def test_gemm_ex_storage_order_validation(L):
+    # gemm_ex(..., a_order, b_order, ab_type, out_type, accumulate)
+    base = (FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1, 0, 0, 0)
+    assert L.gemm_ex(*base, 2, 0, 1, 0, 0, None) == -1
+    assert "a_order=2" in L.fp16mc_last_error().decode()
+    assert L.gemm_ex(*base, 0, -1, 1, 0, 0, None) == -1
+    # A stored K x M needs lda >= M (not K); B stored K x N needs ldb >= N
+    assert L.gemm_ex(FAKE, FAKE, FAKE, 64, 8, 16, 32, 16, 8, 1, 0, 0, 0, 1, 0, 1, 0, 0, None) == -1
+    assert "lda=32 < M=64" in L.fp16mc_last_error().decode()
+    assert L.gemm_ex(FAKE, FAKE, FAKE, 8, 64, 16, 16, 32, 64, 1, 0, 0, 0, 0, 1, 1, 0, 0, None) == -1
+    assert "ldb=32 < N=64" in L.fp16mc_last_error().decode()
+    # ... while lda < K is fine: this call passes the stride checks and stops at the NULL Out
+    assert L.gemm_ex(FAKE, FAKE, 0, 64, 8, 4096, 64, 4096, 8, 1, 0, 0, 0, 1, 0, 1, 0, 0, None) == -1
+    assert "Out is NULL" in L.fp16mc_last_error().decode()
+    # a K x W operand is addressed 64 rows at a time: 2 * 64 * ld must stay below 2^32
+    ld = 1 << 25
+    assert L.gemm_ex(FAKE, FAKE, FAKE, 8192, 8192, 8192, ld, 8192, 8192, 1, 0, 0, 0, 1, 0, 1, 0, 0, None) == -1
+    assert "2^32" in L.fp16mc_last_error().decode()
+
+
+def test_plans_by_storage_order(L):
+    import fp16_matrix_core_amd as f
+    assert f.plan_ex(100, 8, 64).startswith("skinny")
+    for order in ((1, 0), (0, 1), (1, 1)):      # transposed operands never take the skinny kernel
+        assert f.plan_ex(100, 8, 64, 1, *order).startswith("wg128x64")
+        assert f.plan_ex(16, 8, 16, 1, *order).startswith("wave32x32")
+        assert f.plan_ex(8192, 8192, 8192, 1, *order).startswith("wg256x256")
 
 
 def test_gemm_ex_empty_problems(L):

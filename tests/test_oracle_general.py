@@ -1,4 +1,4 @@
-"""Pins of oracle.gemm_ex (bfloat16 operands, accumulation, 16-bit outputs).
+"""Pins of oracle.general (bfloat16 operands, accumulation, 16-bit outputs).
 
 Each pin ties the oracle to something other than itself: the binary32 /
 bfloat16 format definitions, an independent library conversion (torch on the
@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import gemm as og
-from oracle import gemm_ex as ox
+from oracle import general as ox
 from fp16_matrix_core_amd import inputs
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -226,3 +226,45 @@ def test_fp32_rule_unchanged_for_f32_outputs():
         ok2, worst2, nbad2 = ox.within_bound_out(o, ref, bound, "f32")
         assert (ok1, nbad1) == (ok2, nbad2)
         assert worst2 == pytest.approx(worst1 / 1e-4)   # worst is measured against the allowance
+
+
+# ---- storage orders ------------------------------------------------------------------
+
+@pytest.mark.parametrize("a_order,b_order", [("k", "k"), ("k", "mn"), ("mn", "k"), ("mn", "mn")])
+def test_storage_orders_read_the_same_logical_operands(a_order, b_order):
+    """The index formulas (element-by-element gather from padded buffers with NaN
+    gaps) agree with plain transposes, and padding is never read."""
+    rng = np.random.default_rng(23)
+    M, N, K = 7, 5, 9
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    As = A if a_order == "k" else A.T.copy()          # stored array
+    Bs = B if b_order == "k" else B.T.copy()
+    lda, ldb = As.shape[1] + 3, Bs.shape[1] + 5
+    a_flat = np.full(As.shape[0] * lda, np.nan, np.float16)
+    b_flat = np.full(Bs.shape[0] * ldb, np.nan, np.float16)
+    for r in range(As.shape[0]):
+        a_flat[r * lda: r * lda + As.shape[1]] = As[r]
+    for r in range(Bs.shape[0]):
+        b_flat[r * ldb: r * ldb + Bs.shape[1]] = Bs[r]
+    ref_s, bound_s = ox.gemm_ex_strided(a_flat, b_flat, M, N, K, lda, ldb, a_order=a_order, b_order=b_order)
+    ref, bound = ox.gemm_ex(As, Bs, a_order=a_order, b_order=b_order)
+    ref0, bound0 = og.gemm_nt(A, B)
+    assert np.isfinite(ref_s).all()
+    assert np.array_equal(ref_s, ref0) and np.array_equal(ref, ref0)
+    assert np.array_equal(bound_s, bound0) and np.array_equal(bound, bound0)
+
+
+def test_plain_product_reading():
+    """b stored K x N and a K-contiguous: the result is the textbook a @ b (brute force)."""
+    rng = np.random.default_rng(24)
+    a = rng.integers(-4, 5, size=(3, 6)).astype(np.float16)
+    b_kn = rng.integers(-4, 5, size=(6, 4)).astype(np.float16)
+    ref, _ = ox.gemm_ex(a, b_kn, a_order="k", b_order="mn")
+    want = np.zeros((3, 4))
+    for i in range(3):
+        for j in range(4):
+            want[i, j] = sum(float(a[i, k]) * float(b_kn[k, j]) for k in range(6))
+    assert np.array_equal(ref, want)
+    with pytest.raises(ValueError):
+        ox.gemm_ex(a, b_kn, a_order="x")
