@@ -16,7 +16,10 @@
 // between HBM and LDS with 16-byte accesses (one contiguous 8 KiB span),
 // and its fragments move between HBM and VGPRs with each lane's num words in
 // one access (a wavefront touches 256*num contiguous bytes).  The kernel is
-// HBM-bound: 128 bytes read and 128 bytes written per tile.
+// HBM-bound: 128 bytes read and 128 bytes written per tile.  Every HBM access
+// is non-temporal (each byte is touched once; measured +8-11% over cached
+// accesses), and up to 16384 workgroups cover the 2^20-tile workload's 16384
+// blocks in one pass.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -106,7 +109,7 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
     if constexpr (DIR == 0 || DIR == 2) {
       // image: HBM -> LDS
       const u32x4* s = static_cast<const u32x4*>(src) + g0 * (kGroupBytes / 16);
-      for (int c = tid; c < nchunks; c += kThreads) lds_a[c] = s[c];
+      for (int c = tid; c < nchunks; c += kThreads) lds_a[c] = __builtin_nontemporal_load(s + c);
       __syncthreads();
       const unsigned short* img = reinterpret_cast<const unsigned short*>(lds_a);
       for (int lg = hw; lg < ng; lg += kHalfWaves) {
@@ -117,7 +120,7 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
         if constexpr (DIR == 0) {
           // fragment: VGPR -> HBM, lane-major
           W* d = static_cast<W*>(dst) + (g0 + lg) * 32 + l32;
-          *d = v;
+          __builtin_nontemporal_store(v, d);
         } else {
           unsigned short* out = reinterpret_cast<unsigned short*>(lds_b) + lg * kGroupHalves;
 #pragma unroll
@@ -127,14 +130,14 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
       if constexpr (DIR == 2) {
         __syncthreads();
         u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
-        for (int c = tid; c < nchunks; c += kThreads) d[c] = lds_b[c];
+        for (int c = tid; c < nchunks; c += kThreads) __builtin_nontemporal_store(lds_b[c], d + c);
       }
       __syncthreads();
     } else {
       // fragment: HBM -> VGPR -> LDS image
       unsigned short* img = reinterpret_cast<unsigned short*>(lds_a);
       for (int lg = hw; lg < ng; lg += kHalfWaves) {
-        const W v = *(static_cast<const W*>(src) + (g0 + lg) * 32 + l32);
+        const W v = __builtin_nontemporal_load(static_cast<const W*>(src) + (g0 + lg) * 32 + l32);
 #pragma unroll
         for (int t = 0; t < NUM; ++t)
           lds_write_word<NUM, COL>(img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
@@ -142,7 +145,7 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
       __syncthreads();
       // image: LDS -> HBM
       u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
-      for (int c = tid; c < nchunks; c += kThreads) d[c] = lds_a[c];
+      for (int c = tid; c < nchunks; c += kThreads) __builtin_nontemporal_store(lds_a[c], d + c);
       __syncthreads();
     }
   }
@@ -152,7 +155,7 @@ template <int NUM, bool COL, int DIR>
 hipError_t launch_one(const void* src, void* dst, int64_t groups, hipStream_t stream) {
   constexpr int kGroupsPerBlock = kBlockBytes / (128 * NUM);
   int64_t nblocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  const int64_t grid = nblocks < 4096 ? nblocks : 4096;
+  const int64_t grid = nblocks < 16384 ? nblocks : 16384;
   void* args[] = {const_cast<void**>(&src), &dst, &groups, &nblocks};
   return hipLaunchKernel(reinterpret_cast<const void*>(&frag_copy_kernel<NUM, COL, DIR>),
                          dim3(static_cast<unsigned>(grid)), dim3(kThreads), args, 0, stream);
