@@ -54,7 +54,6 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Operand element types.  Both move through the kernels as raw 16-bit
@@ -64,17 +63,11 @@ struct InF16 {
   static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
 };
 struct InBF16 {
   typedef bf16x8 V8;
   static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 
@@ -91,8 +84,12 @@ __device__ __forceinline__ void store_out(OutT* p, float v) {
 // of BK (32 or 64) held in a ring of STAGES LDS stages; WAVES_PER_SIMD
 // workgroups' worth of wavefronts share each SIMD (the register budget
 // follows from it).
-template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_, int BK_ = 32>
+template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_, int BK_ = 32,
+          int STREAM_ = 0>
 struct Cfg {
+  // STREAM bit 0 / bit 1: A's / B's tiles are read by one workgroup only, so
+  // their direct loads are non-temporal (no reuse to keep them cached for).
+  static constexpr int STREAM = STREAM_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
   static constexpr int BK = BK_;
   using Swz = LdsSwizzle<2 * BK_>;
@@ -123,6 +120,15 @@ using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
 // 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
 using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64>;
+// Tall 64x32 tiles for N <= 32: the product streams A (read by one
+// workgroup each, non-temporal) against a B that every workgroup shares.
+// 16384x8x16384: 93 us against 118 us for a dedicated register-streaming
+// kernel with 16x16x32 MFMAs (full-line direct loads and the streaming hint
+// make the difference).
+using CfgTall = Cfg<64, 32, 2, 1, 1, 4, 1, 64, 1>;
+// The 128x64 tiles with both operands streamed, for problems that are one
+// tile each (batches of small products): 4096 x 128x64x64 47.6 -> 44.6 us.
+using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 3>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -142,9 +148,11 @@ __device__ __forceinline__ u32x4 load_chunk_masked(const unsigned short* row, in
 
 // 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
 // lane l's bytes land at lds_span + 16 l; `lds_span` and `soff` are uniform.
+// NT = true sets the non-temporal hint.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned char* lds_span, unsigned voff,
                                       unsigned soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_span, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_span, 16, voff, soff, 0, NT ? 2 : 0);
 }
 
 // 8 consecutive-K values of one M for an MFMA operand from a transposed
@@ -301,24 +309,25 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     return make_rsrc(tile + k0 * ld, static_cast<unsigned>(2 * (rows - 1) * ld + last));
   };
   constexpr int kLoads = C::A_LOADS + C::B_LOADS;   // direct loads per slice per wavefront
+  constexpr bool kNtA = (C::STREAM & 1) != 0, kNtB = (C::STREAM & 2) != 0;
   // All direct loads of slice `slice` (A's, then B's).
   auto dma_all = [&](unsigned char* as, unsigned char* bs, int64_t slice) {
     const unsigned koff = static_cast<unsigned>(2 * C::BK * slice);
     if constexpr (!A_MN) {
 #pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q) dma16(a_rsrc, as + span(q), a_off[q], koff);
+      for (int q = 0; q < C::A_LOADS; ++q) dma16<kNtA>(a_rsrc, as + span(q), a_off[q], koff);
     } else {
       const __amdgpu_buffer_rsrc_t r = slice_rsrc(a_tile, lda, M - i0, slice);
 #pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q) dma16(r, as + span(q), a_off[q], 0);
+      for (int q = 0; q < C::A_LOADS; ++q) dma16<kNtA>(r, as + span(q), a_off[q], 0);
     }
     if constexpr (!B_MN) {
 #pragma unroll
-      for (int q = 0; q < C::B_LOADS; ++q) dma16(b_rsrc, bs + span(q), b_off[q], koff);
+      for (int q = 0; q < C::B_LOADS; ++q) dma16<kNtB>(b_rsrc, bs + span(q), b_off[q], koff);
     } else {
       const __amdgpu_buffer_rsrc_t r = slice_rsrc(b_tile, ldb, N - j0, slice);
 #pragma unroll
-      for (int q = 0; q < C::B_LOADS; ++q) dma16(r, bs + span(q), b_off[q], 0);
+      for (int q = 0; q < C::B_LOADS; ++q) dma16<kNtB>(r, bs + span(q), b_off[q], 0);
     }
   };
   // Last, partial K slice (index nfull): K-contiguous operands through
@@ -336,7 +345,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     } else {
       const __amdgpu_buffer_rsrc_t r = slice_rsrc(a_tile, lda, M - i0, slice);
 #pragma unroll
-      for (int p = 0; p < C::A_LOADS; ++p) dma16(r, as + span(p), a_off[p], 0);
+      for (int p = 0; p < C::A_LOADS; ++p) dma16<kNtA>(r, as + span(p), a_off[p], 0);
     }
     if constexpr (!B_MN) {
 #pragma unroll
@@ -349,7 +358,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     } else {
       const __amdgpu_buffer_rsrc_t r = slice_rsrc(b_tile, ldb, N - j0, slice);
 #pragma unroll
-      for (int p = 0; p < C::B_LOADS; ++p) dma16(r, bs + span(p), b_off[p], 0);
+      for (int p = 0; p < C::B_LOADS; ++p) dma16<kNtB>(r, bs + span(p), b_off[p], 0);
     }
   };
 
@@ -595,133 +604,6 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   }
 }
 
-// ---------------------------------------------------------------------------
-// Skinny products (N <= 16): Out (M x N) = A (M x K) @ B (N x K)^T.
-// The work is a stream over A (each element used once), so A bypasses LDS:
-// every lane loads four 16-byte chunks of one row per 128-wide K block (the
-// four lanes of a row cover its 256 bytes), and B -- padded with zero
-// columns to 16 -- is loaded in the same K order, which is all the MFMA
-// needs (any K order gives the same sum as long as both operands agree).
-// v_mfma_f32_16x16x32_f16: lane l supplies row/column l%16 and 8 fp16 of K;
-// here lane (r = l%16, q = l/16) of MFMA step j uses K elements
-// kb + 32j + 8q .. +8 of its row, so each load instruction covers 64
-// contiguous bytes of 16 rows (a quarter-line per lane scattered over 256
-// bytes measured 29% slower).  The last, partial block uses K elements
-// kb + 32q + 8j instead (any order works while A and B agree).  Eight
-// wavefronts split K; their partial 64 x 16 results are summed through LDS.
-// ---------------------------------------------------------------------------
-constexpr int kSkRows = 64;        // output rows per workgroup (4 MFMA row tiles)
-constexpr int kSkWaves = 8;        // wavefronts splitting K
-constexpr int kSkBlock = 128;      // K per block per wavefront
-
-// Four 16-byte chunks of a row at elements k + 32 j (all inside K).  With
-// k = kb + 8q the four lanes of a row read 64 contiguous bytes per load.
-__device__ __forceinline__ void sk_load(const unsigned short* row, int64_t k, u32x4 (&v)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const u32x4*>(row + k + 32 * j);
-}
-// The same with zeros past K (the last, partial block only).
-__device__ __forceinline__ void sk_load_masked(const unsigned short* row, int64_t k, int64_t K, u32x4 (&v)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = load_chunk_masked(row, k + 8 * j, K);
-}
-
-template <class In, class OutT, bool ACC>
-__global__ void __launch_bounds__(kSkWaves * 64, 1)
-gemm_nt_skinny_kernel(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B,
-                      OutT* __restrict__ Out,
-                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
-                      int64_t sA, int64_t sB, int64_t sO, int64_t tiles_m) {
-  __shared__ float red[kSkWaves][kSkRows][16];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t b = blockIdx.x / static_cast<uint32_t>(tiles_m);
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x - b * static_cast<uint32_t>(tiles_m)) * kSkRows;
-  A += b * sA;
-  B += b * sB;
-  Out += b * sO;
-
-  const int r = mfma16::operand_row(lane);   // row in a 16-row tile / column of B
-  const int q = lane >> 4;                   // 32-element quarter of the block
-  const unsigned short* arow[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t i = i0 + 16 * t + r;
-    arow[t] = A + (i < M ? i : M - 1) * lda;
-  }
-  // lanes past N read row N-1 (in bounds) and zero it: no divergent branch
-  const bool has_b = r < N;
-  const unsigned short* brow = B + (has_b ? r : N - 1) * ldb;
-  const unsigned bmask = has_b ? 0xFFFFFFFFu : 0u;
-
-  // Full 128-wide K blocks are split evenly over the wavefronts; the last,
-  // partial block (if any) goes to the last wavefront with masked loads.
-  const int64_t nfull = K / kSkBlock;
-  const int64_t per = (nfull + kSkWaves - 1) / kSkWaves;
-  const int64_t blk0 = wave * per < nfull ? wave * per : nfull;
-  const int64_t blk1 = (blk0 + per < nfull) ? blk0 + per : nfull;
-
-  f32x4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4{};
-  u32x4 va[2][4][4];
-  u32x4 vb[2][4];
-  auto load = [&](int buf, int64_t blk) {
-    const int64_t k = blk * kSkBlock + 8 * q;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sk_load(arow[t], k, va[buf][t]);
-    sk_load(brow, k, vb[buf]);
-  };
-  auto mma = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const typename In::V8 bj = __builtin_bit_cast(typename In::V8, vb[buf][j] & bmask);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = In::mfma16(__builtin_bit_cast(typename In::V8, va[buf][t][j]), bj, acc[t]);
-    }
-  };
-  if (blk0 < blk1) {
-    load(0, blk0);
-    int64_t blk = blk0;
-    for (; blk + 2 < blk1; blk += 2) {  // blocks blk+1 and blk+2 exist: no branch in the body
-      load(1, blk + 1);
-      mma(0);
-      load(0, blk + 2);
-      mma(1);
-    }
-    if (blk + 1 < blk1) {
-      load(1, blk + 1);
-      mma(0);
-      mma(1);
-    } else {
-      mma(0);
-    }
-  }
-  if (K % kSkBlock != 0 && wave == kSkWaves - 1) {
-    const int64_t k = nfull * kSkBlock + 32 * q;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sk_load_masked(arow[t], k, K, va[0][t]);
-    sk_load_masked(brow, k, K, vb[0]);
-    mma(0);
-  }
-
-  // partial sums -> LDS: element v of lane l in row tile t is (row 16t + 4(l/16) + v, column l%16)
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][16 * t + mfma16::acc_row(lane, v)][mfma16::acc_col(lane, v)] = acc[t][v];
-  __syncthreads();
-  for (int e = threadIdx.x; e < kSkRows * 16; e += kSkWaves * 64) {
-    const int row = e / 16, col = e % 16;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) sum += red[w][row][col];
-    const int64_t i = i0 + row;
-    if (i < M && col < N) store_out<OutT, ACC>(Out + i * ldo + col, sum);
-  }
-}
-
 template <class C>
 int64_t tiles_of(int64_t M, int64_t N, int64_t batch, int64_t* tm, int64_t* tn) {
   *tm = (M + C::BM - 1) / C::BM;
@@ -742,19 +624,6 @@ hipError_t launch(const GemmProblem& p, hipStream_t stream) {
                   const_cast<int64_t*>(&total)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_kernel<C, In, OutT, ACC, A_MN, B_MN>),
                          dim3(static_cast<unsigned>(total)), dim3(C::NT), args, 0, stream);
-}
-
-template <class In, class OutT, bool ACC>
-hipError_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
-  const unsigned short* A = static_cast<const unsigned short*>(p.A);
-  const unsigned short* B = static_cast<const unsigned short*>(p.B);
-  OutT* Out = static_cast<OutT*>(p.Out);
-  int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldo = p.ldo;
-  int64_t sA = p.sA, sB = p.sB, sO = p.sO;
-  int64_t tiles_m = (M + kSkRows - 1) / kSkRows;
-  void* args[] = {&A, &B, &Out, &M, &N, &K, &lda, &ldb, &ldo, &sA, &sB, &sO, &tiles_m};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_nt_skinny_kernel<In, OutT, ACC>),
-                         dim3(static_cast<unsigned>(tiles_m * p.batch)), dim3(kSkWaves * 64), args, 0, stream);
 }
 
 template <class T>
@@ -783,12 +652,6 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   });
 }
 
-hipError_t launch_skinny_typed(const GemmProblem& p, hipStream_t stream) {
-  return with_types(p, [&](auto in, auto out, auto acc) {
-    return launch_skinny<typename decltype(in)::type, typename decltype(out)::type, decltype(acc)::value>(p, stream);
-  });
-}
-
 template <class C>
 int64_t plan_tiles(int64_t M, int64_t N, int64_t batch) {
   int64_t tm, tn;
@@ -802,9 +665,8 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
     case GemmPlan::kWave32: return launch_cfg<CfgWave32, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64: return launch_cfg<CfgWg128x64, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg256: return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
-    case GemmPlan::kSkinny:
-      if constexpr (!A_MN && !B_MN) return launch_skinny_typed(p, stream);
-      return hipErrorInvalidValue;   // the plan logic never picks it for transposed operands
+    case GemmPlan::kTall: return launch_cfg<CfgTall, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x64Stream: return launch_cfg<CfgWg128x64Stream, A_MN, B_MN>(p, stream);
     default: return hipSuccess;
   }
 }

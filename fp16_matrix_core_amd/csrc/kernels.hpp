@@ -33,9 +33,10 @@ struct GemmProblem {
 enum class GemmPlan : int {
   kNone = 0,      // empty problem, nothing to launch
   kWave32 = 1,    // one wavefront per 32x32 output tile (tiny problems)
-  kWg128x64 = 2,  // 4 wavefronts per 128x64 tile (small, batched, mid-size)
-  kWg256 = 3,     // 4 wavefronts per 256x256 tile (large problems)
-  kSkinny = 4,    // N <= 16: 8 wavefronts split K over 64 rows, A streamed past LDS
+  kWg128x64 = 2,        // 4 wavefronts per 128x64 tile (small and mid-size)
+  kWg256 = 3,           // 4 wavefronts per 256x256 tile (large problems)
+  kTall = 4,            // N <= 32: 2 wavefronts per 64x32 tile, A streamed
+  kWg128x64Stream = 5,  // batches of one-tile problems: 128x64 tiles, both operands streamed
 };
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool a_mn, bool b_mn);

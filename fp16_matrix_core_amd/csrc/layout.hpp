@@ -5,7 +5,6 @@
 //                 rows that hold a 32- or 64-element fp16 K slice of an
 //                 operand tile.
 //   mfma32        lane maps of v_mfma_f32_32x32x16_f16.
-//   mfma16        lane maps of v_mfma_f32_16x16x32_f16.
 //   m8n8          the 8x8 b16 matrix fragment of the warp-collective matrix
 //                 load/store, mapped onto 64-lane wavefronts.
 //
@@ -119,20 +118,6 @@ FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 5) + e;
 FP16MC_HD constexpr int acc_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 31; }
 }  // namespace mfma32
-
-// ---------------------------------------------------------------------------
-// v_mfma_f32_16x16x32_f16: D(16x16) += X(16x32) * Y(32x16).
-// Operands: lane l supplies X row (l % 16) / Y column (l % 16) at
-// k = 8*(l / 16) + e.  Accumulator: 4 fp32 per lane, element v of lane l is
-// D[4*(l/16) + v][l % 16].
-// ---------------------------------------------------------------------------
-namespace mfma16 {
-constexpr int kM = 16, kN = 16, kK = 32, kAcc = 4;
-FP16MC_HD constexpr int operand_row(int lane) { return lane & 15; }
-FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 4) + e; }
-FP16MC_HD constexpr int acc_row(int lane, int v) { return 4 * (lane >> 4) + v; }
-FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 15; }
-}  // namespace mfma16
 
 // ---------------------------------------------------------------------------
 // m8n8 fragment of the matrix load/store: over a 32-lane group, lane l holds

@@ -194,16 +194,6 @@ int main() {
       for (int e = 0; e < 8; ++e) ops.insert({mfma32::operand_row(l), mfma32::operand_k(l, e)});
     CHECK(ops.size() == 32 * 16, "mfma32 operand map not a bijection");
   }
-  {
-    std::set<std::pair<int, int>> cells;
-    for (int l = 0; l < 64; ++l)
-      for (int v = 0; v < mfma16::kAcc; ++v) cells.insert({mfma16::acc_row(l, v), mfma16::acc_col(l, v)});
-    CHECK(cells.size() == 16 * 16, "mfma16 accumulator map not a bijection");
-    std::set<std::pair<int, int>> ops;
-    for (int l = 0; l < 64; ++l)
-      for (int e = 0; e < 8; ++e) ops.insert({mfma16::operand_row(l), mfma16::operand_k(l, e)});
-    CHECK(ops.size() == 16 * 32, "mfma16 operand map not a bijection");
-  }
   // m8n8: each 32-lane half covers the 8 rows x 4 column pairs once; images are bijections
   for (int num : {1, 2, 4})
     for (int col = 0; col < 2; ++col) {

@@ -215,29 +215,30 @@ def test_batched_equals_single_calls(f):
 
 
 def test_skinny(f):
-    """M = 16384, N = 8, K = 16384 (seed 5); every element checked."""
+    """M = 16384, N = 8, K = 16384 (seed 5) on the tall tiles; every element checked."""
     A, B = inputs.skinny()
-    assert f.plan(16384, 8, 16384).startswith("skinny")
+    assert f.plan(16384, 8, 16384).startswith("tall64x32")
     got, pad = _run(f, A, B, ldo_pad=3)
     _assert_parity(got, A, B)
     assert np.isnan(pad).all()
 
 
-SKINNY = [(64, 1, 128), (65, 8, 129), (1000, 16, 1000), (33, 3, 7), (4097, 5, 2048), (200, 16, 0), (128, 12, 4100)]
+SKINNY = [(64, 1, 128), (65, 8, 129), (1000, 16, 1000), (33, 3, 7), (4097, 5, 2048), (200, 16, 0), (128, 12, 4100),
+          (500, 32, 300), (301, 24, 100), (70, 17, 64)]
 
 
 @pytest.mark.parametrize("shape", SKINNY, ids=lambda s: "x".join(map(str, s)))
 def test_skinny_ragged(f, shape):
-    """N <= 16 shapes on the skinny kernel: ragged M, N, K (incl. K = 0 and K not a multiple of 8)."""
+    """N <= 32 shapes on the tall tiles: ragged M, N, K (incl. K = 0 and K not a multiple of 8)."""
     M, N, K = shape
-    assert f.plan(M, N, K).startswith("skinny") or (M <= 32 and N <= 32)
+    assert f.plan(M, N, K).startswith("tall64x32") or (M <= 32 and N <= 32)
     rng = np.random.default_rng(M + 31 * N + 7 * K)
     A = inputs.uniform_f16((M, K), rng)
     B = inputs.uniform_f16((N, K), rng)
     if K == 0:
-        out = torch.full((M, 16), SENTINEL, dtype=torch.float32, device="cuda")
+        out = torch.full((M, 36), SENTINEL, dtype=torch.float32, device="cuda")
         a = torch.empty(8, dtype=torch.float16, device="cuda")
-        f.gemm_nt_raw(a.data_ptr(), a.data_ptr(), out.data_ptr(), M, N, 0, 8, 8, 16,
+        f.gemm_nt_raw(a.data_ptr(), a.data_ptr(), out.data_ptr(), M, N, 0, 8, 8, 36,
                       torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         full = out.cpu().numpy()

@@ -138,9 +138,9 @@ def test_gemm_ex_storage_order_validation(L):
 
 def test_plans_by_storage_order(L):
     import fp16_matrix_core_amd as f
-    assert f.plan_ex(100, 8, 64).startswith("skinny")
-    for order in ((1, 0), (0, 1), (1, 1)):      # transposed operands never take the skinny kernel
-        assert f.plan_ex(100, 8, 64, 1, *order).startswith("wg128x64")
+    for order in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        assert f.plan_ex(100, 8, 64, 1, *order).startswith("tall64x32")
+        assert f.plan_ex(100, 40, 64, 1, *order).startswith("wg128x64_")
         assert f.plan_ex(16, 8, 16, 1, *order).startswith("wave32x32")
         assert f.plan_ex(8192, 8192, 8192, 1, *order).startswith("wg256x256")
 
@@ -177,12 +177,13 @@ def test_plans(L):
     import fp16_matrix_core_amd as f
     assert f.plan(0, 8, 8) is None
     assert f.plan(16, 8, 16).startswith("wave32x32")
-    assert f.plan(128, 64, 64).startswith("wg128x64")
-    assert f.plan(128, 64, 64, 4096).startswith("wg128x64")
+    assert f.plan(128, 64, 64).startswith("wg128x64_")
+    assert f.plan(128, 64, 64, 4096).startswith("wg128x64s_")      # one-tile problems: streamed
+    assert f.plan(129, 64, 64, 4096).startswith("wg128x64_")
     assert f.plan(8192, 8192, 8192).startswith("wg256x256")
-    assert f.plan(16384, 8, 16384).startswith("skinny")
-    assert f.plan(100, 16, 64).startswith("skinny")
-    assert f.plan(100, 17, 64).startswith("wg128x64")
+    assert f.plan(16384, 8, 16384).startswith("tall64x32")
+    assert f.plan(100, 32, 64).startswith("tall64x32")
+    assert f.plan(100, 33, 64).startswith("wg128x64_")
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
