@@ -16,6 +16,7 @@ while that hash still matches.
 """
 
 import argparse
+import re
 import csv
 import os
 import statistics
@@ -29,6 +30,34 @@ COPY_MATCH = "copyBuffer"
 def _rows(path):
     with open(path, newline="") as fh:
         return list(csv.DictReader(fh))
+
+
+_OUT_TYPES = {"f": "float", "DF16_": "_Float16", "DF16b": "__bf16"}
+
+
+def short_name(name):
+    """A kernel name without namespaces and parameter lists.
+
+    The profiler demangles most names; ones whose template arguments include
+    _Float16 or __bf16 stay mangled, and the product kernels among them are
+    spelled out here from their template arguments.
+    """
+    m = re.match(r"_ZN6fp16mc12_GLOBAL__N_114gemm_nt_kernelINS0_3CfgI((?:Li\d+E)+)EENS0_\d+(In\w+?)E"
+                 r"(f|DF16_|DF16b)((?:Lb[01]E)+)", name)
+    if m:
+        cfg = ", ".join(re.findall(r"Li(\d+)E", m.group(1)))
+        flags = ", ".join("true" if b == "1" else "false" for b in re.findall(r"Lb([01])E", m.group(4)))
+        return f"gemm_nt_kernel<Cfg<{cfg}>, {m.group(2)}, {_OUT_TYPES[m.group(3)]}, {flags}>"
+    n = name.replace("void ", "", 1).replace("fp16mc::(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):          # drop the parameter list after the template arguments
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and i > 0:
+            return n[:i]
+    return n
 
 
 def kernel_stats(path, match=None):
@@ -86,10 +115,12 @@ def main(argv=None):
     stamp = time.strftime("%Y-%m-%d")
     if a.cmd == "stats":
         ks = kernel_stats(a.csv, a.match)
-        lines = [f"# rocprofv3 kernel statistics ({stamp})", f"# command: {a.command}", "",
+        lines = [f"# rocprofv3 kernel statistics ({stamp})", f"# command: {a.command}",
+                 "# gemm_nt_kernel<tile configuration, operand type, output type, accumulate,"
+                 " A stored K x M, B stored K x N>", "",
                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for k in sorted(ks, key=lambda k: -k["avg_ns"] * k["calls"]):
-            lines.append(f"| `{k['name'][:110]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
+            lines.append(f"| `{short_name(k['name'])[:160]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
                          f"{k['min_ns'] / 1e3:.2f} | {k['max_ns'] / 1e3:.2f} |")
         text = "\n".join(lines) + "\n"
     else:
