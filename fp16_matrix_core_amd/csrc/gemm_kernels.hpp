@@ -129,6 +129,13 @@ using CfgTall = Cfg<64, 32, 2, 1, 1, 4, 1, 64, 1>;
 // The 128x64 tiles with both operands streamed, for problems that are one
 // tile each (batches of small products): 4096 x 128x64x64 47.6 -> 44.6 us.
 using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 3>;
+// Intermediate tiles for problems too small to fill the 256 CUs with
+// 256x256 tiles: 256x128 (three 48 KiB stages) and 128x128 (two 32 KiB
+// stages, two workgroups per CU).
+using CfgWg256x128 = Cfg<256, 128, 2, 2, 4, 3, 1, 64>;
+using CfgWg128x128 = Cfg<128, 128, 2, 2, 8, 2, 2, 64>;
+// Wide 32x64 tiles for M <= 32: the mirror of the tall tiles, B streamed.
+using CfgWide = Cfg<32, 64, 1, 2, 1, 4, 1, 64, 2>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -667,6 +674,9 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
     case GemmPlan::kWg256: return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
     case GemmPlan::kTall: return launch_cfg<CfgTall, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64Stream: return launch_cfg<CfgWg128x64Stream, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256x128: return launch_cfg<CfgWg256x128, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x128: return launch_cfg<CfgWg128x128, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWide: return launch_cfg<CfgWide, A_MN, B_MN>(p, stream);
     default: return hipSuccess;
   }
 }

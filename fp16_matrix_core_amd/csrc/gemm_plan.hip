@@ -2,22 +2,67 @@
 // problem gets, its grid, its addressing limits, and the dispatch to the
 // source file that instantiates the operands' storage order.
 
+#include <cmath>
+
 #include "gemm_kernels.hpp"
 
 namespace fp16mc {
 
-GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t /*K*/, int64_t batch, bool /*a_mn*/, bool /*b_mn*/) {
+namespace {
+
+// Measured on MI355X (fp16 -> fp32, NT, whole chip busy): each tile
+// configuration's rate with every CU occupied, the K at which its per-tile
+// prologue and epilogue cost as much as the K loop, and how many workgroups
+// fit on a CU.
+struct TileModel {
+  GemmPlan plan;
+  int bm, bn;
+  double tflops;     // rate at full occupancy, K >> k0
+  double k0;         // per-tile overhead expressed in K
+  int per_cu;        // workgroups per CU (LDS)
+};
+constexpr TileModel kModels[] = {
+    {GemmPlan::kWg256, 256, 256, 1244.0, 600.0, 1},
+    {GemmPlan::kWg256x128, 256, 128, 1150.0, 450.0, 1},
+    {GemmPlan::kWg128x128, 128, 128, 1060.0, 200.0, 2},
+    {GemmPlan::kWg128x64, 128, 64, 870.0, 220.0, 2},
+};
+
+// Predicted useful rate: the full-occupancy rate, discounted for the
+// per-tile overhead, for idle CUs in the last wave of tiles, and for the part
+// of the edge tiles that lies outside M x N.  A partly filled chip runs at a
+// higher clock (the product is power-limited), hence the 0.75 power on the
+// fill fraction (fitted to the measured rates).
+double predicted_rate(const TileModel& m, int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const int64_t tm = (M + m.bm - 1) / m.bm, tn = (N + m.bn - 1) / m.bn;
+  const double tiles = double(tm) * double(tn) * double(batch);
+  const double slots = 256.0 * m.per_cu;
+  const double waves = std::ceil(tiles / slots);
+  const double fill = tiles / (waves * slots);
+  const double useful = (double(M) / double(tm * m.bm)) * (double(N) / double(tn * m.bn));
+  return m.tflops * (double(K) / (double(K) + m.k0)) * std::pow(fill, 0.75) * useful;
+}
+
+}  // namespace
+
+GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool /*a_mn*/, bool /*b_mn*/) {
   if (M <= 0 || N <= 0 || batch <= 0) return GemmPlan::kNone;
   if (M <= 32 && N <= 32) return GemmPlan::kWave32;
-  // N <= 32: one column of tall tiles streams A past a shared B
+  // N <= 32: one column of tall tiles streams A past a shared B; M <= 32: the mirror
   if (N <= 32) return GemmPlan::kTall;
-  // 256x256 tiles only where they are mostly full and there are enough of
-  // them to occupy at least half of the 256 CUs.
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256) * batch;
-  if (M >= 256 && N >= 256 && big_tiles >= 128) return GemmPlan::kWg256;
+  if (M <= 32) return GemmPlan::kWide;
   // a batch of one-tile problems: nothing is read twice
   if (batch > 1 && M <= 128 && N <= 64) return GemmPlan::kWg128x64Stream;
-  return GemmPlan::kWg128x64;
+  GemmPlan best = GemmPlan::kWg128x64;
+  double best_rate = -1.0;
+  for (const TileModel& m : kModels) {
+    const double r = predicted_rate(m, M, N, K > 0 ? K : 1, batch);
+    if (r > best_rate) {
+      best_rate = r;
+      best = m.plan;
+    }
+  }
+  return best;
 }
 
 const char* gemm_plan_name(GemmPlan plan) {
@@ -27,6 +72,9 @@ const char* gemm_plan_name(GemmPlan plan) {
     case GemmPlan::kWg256: return "wg256x256_w4_mfma32x32x16";
     case GemmPlan::kTall: return "tall64x32_w2_mfma32x32x16";
     case GemmPlan::kWg128x64Stream: return "wg128x64s_w4_mfma32x32x16";
+    case GemmPlan::kWg256x128: return "wg256x128_w4_mfma32x32x16";
+    case GemmPlan::kWg128x128: return "wg128x128_w4_mfma32x32x16";
+    case GemmPlan::kWide: return "wide32x64_w2_mfma32x32x16";
     default: return nullptr;
   }
 }
@@ -39,6 +87,9 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
     case GemmPlan::kWg256: return tiles_of<CfgWg256>(M, N, batch, &tm, &tn);
     case GemmPlan::kTall: return tiles_of<CfgTall>(M, N, batch, &tm, &tn);
     case GemmPlan::kWg128x64Stream: return tiles_of<CfgWg128x64Stream>(M, N, batch, &tm, &tn);
+    case GemmPlan::kWg256x128: return tiles_of<CfgWg256x128>(M, N, batch, &tm, &tn);
+    case GemmPlan::kWg128x128: return tiles_of<CfgWg128x128>(M, N, batch, &tm, &tn);
+    case GemmPlan::kWide: return tiles_of<CfgWide>(M, N, batch, &tm, &tn);
     default: return 0;
   }
 }
@@ -61,6 +112,9 @@ bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, 
     case GemmPlan::kWg256: return fits_offsets<CfgWg256>(K, lda, ldb, a_mn, b_mn);
     case GemmPlan::kTall: return fits_offsets<CfgTall>(K, lda, ldb, a_mn, b_mn);
     case GemmPlan::kWg128x64Stream: return fits_offsets<CfgWg128x64Stream>(K, lda, ldb, a_mn, b_mn);
+    case GemmPlan::kWg256x128: return fits_offsets<CfgWg256x128>(K, lda, ldb, a_mn, b_mn);
+    case GemmPlan::kWg128x128: return fits_offsets<CfgWg128x128>(K, lda, ldb, a_mn, b_mn);
+    case GemmPlan::kWide: return fits_offsets<CfgWide>(K, lda, ldb, a_mn, b_mn);
     default: return true;
   }
 }

@@ -37,6 +37,9 @@ enum class GemmPlan : int {
   kWg256 = 3,           // 4 wavefronts per 256x256 tile (large problems)
   kTall = 4,            // N <= 32: 2 wavefronts per 64x32 tile, A streamed
   kWg128x64Stream = 5,  // batches of one-tile problems: 128x64 tiles, both operands streamed
+  kWg256x128 = 6,       // 4 wavefronts per 256x128 tile
+  kWg128x128 = 7,       // 4 wavefronts per 128x128 tile, two workgroups per CU
+  kWide = 8,            // M <= 32: 2 wavefronts per 32x64 tile, B streamed
 };
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool a_mn, bool b_mn);

@@ -88,14 +88,15 @@ def test_permutation_b_exact(f):
     assert np.array_equal(got, A.astype(np.float32)[:, perm])
 
 
-def test_permutation_large_tiles_exact(f):
-    """A permutation product on the 256x256 configuration: any lane-map mistake permutes the output."""
+@pytest.mark.parametrize("M,N,plan", [(4096, 3072, "wg256x256"), (8192, 3072, "wg256x128"),
+                                      (8192, 1024, "wg128x128")])
+def test_permutation_large_tiles_exact(f, M, N, plan):
+    """A permutation product on each large-tile configuration: any lane-map mistake permutes the output."""
     rng = np.random.default_rng(21)
-    M, N = 8192, 1024
     A = inputs.uniform_f16((M, N), rng)
     perm = rng.permutation(N)
     P = inputs.permutation_f16(perm)
-    assert f.plan(M, N, N).startswith("wg256")
+    assert f.plan(M, N, N).startswith(plan)
     got, _ = _run(f, A, P)
     assert np.array_equal(got, A.astype(np.float32)[:, perm])
 

@@ -181,6 +181,11 @@ def test_plans(L):
     assert f.plan(128, 64, 64, 4096).startswith("wg128x64s_")      # one-tile problems: streamed
     assert f.plan(129, 64, 64, 4096).startswith("wg128x64_")
     assert f.plan(8192, 8192, 8192).startswith("wg256x256")
+    assert f.plan(8192, 1024, 8192).startswith("wg256x128")    # 256x256 tiles would fill half the CUs
+    assert f.plan(8192, 8192, 1024).startswith("wg128x128")    # short K: two workgroups per CU
+    assert f.plan(2048, 2048, 2048).startswith("wg128x64_")
+    assert f.plan(16384, 64, 4096).startswith("wg128x64_")     # 256-wide tiles would be 3/4 empty
+    assert f.plan(8, 16384, 16384).startswith("wide32x64")
     assert f.plan(16384, 8, 16384).startswith("tall64x32")
     assert f.plan(100, 32, 64).startswith("tall64x32")
     assert f.plan(100, 33, 64).startswith("wg128x64_")
