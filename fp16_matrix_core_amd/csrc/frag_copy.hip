@@ -134,13 +134,28 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
       }
       __syncthreads();
     } else {
-      // fragment: HBM -> VGPR -> LDS image
+      // fragment: HBM -> VGPR -> LDS image.  In a full block every half-wave
+      // loads all its fragments before writing any, so that its loads (num
+      // words per lane each) are in flight together.
       unsigned short* img = reinterpret_cast<unsigned short*>(lds_a);
-      for (int lg = hw; lg < ng; lg += kHalfWaves) {
-        const W v = __builtin_nontemporal_load(static_cast<const W*>(src) + (g0 + lg) * 32 + l32);
+      const W* frag = static_cast<const W*>(src) + g0 * 32 + l32;
+      if (ng == kGroupsPerBlock) {
+        constexpr int kIt = kGroupsPerBlock / kHalfWaves;
+        W v[kIt];
 #pragma unroll
-        for (int t = 0; t < NUM; ++t)
-          lds_write_word<NUM, COL>(img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
+        for (int i = 0; i < kIt; ++i) v[i] = __builtin_nontemporal_load(frag + (hw + i * kHalfWaves) * 32);
+#pragma unroll
+        for (int i = 0; i < kIt; ++i)
+#pragma unroll
+          for (int t = 0; t < NUM; ++t)
+            lds_write_word<NUM, COL>(img + (hw + i * kHalfWaves) * kGroupHalves, l32, t, Words<NUM>::get(v[i], t));
+      } else {
+        for (int lg = hw; lg < ng; lg += kHalfWaves) {
+          const W v = __builtin_nontemporal_load(frag + lg * 32);
+#pragma unroll
+          for (int t = 0; t < NUM; ++t)
+            lds_write_word<NUM, COL>(img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
+        }
       }
       __syncthreads();
       // image: LDS -> HBM
