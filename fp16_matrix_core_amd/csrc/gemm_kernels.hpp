@@ -130,9 +130,11 @@ using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
 // kernel with 16x16x32 MFMAs (full-line direct loads and the streaming hint
 // make the difference).
 using CfgTall = Cfg<64, 32, 2, 1, 1, 4, 1, 64, 1>;
-// The 128x64 tiles with both operands streamed, for problems that are one
-// tile each (batches of small products): 4096 x 128x64x64 47.6 -> 44.6 us.
-using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 3>;
+// The 128x64 tiles with operands and output streamed, for problems that are
+// one tile each (batches of small products; each workgroup reads and writes
+// its own data once): two 24 KiB stages, so more workgroups share a CU.
+// 4096 x 128x64x64: 47 -> 43 us.
+using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 2, 2, 64, 7>;
 // Intermediate tiles for problems too small to fill the 256 CUs with
 // 256x256 tiles: 256x128 (three 48 KiB stages) and 128x128 (two 32 KiB
 // stages, two workgroups per CU).
