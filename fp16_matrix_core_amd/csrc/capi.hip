@@ -100,7 +100,7 @@ int gemm_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64
                                    (long long)grid, (long long)kMaxGrid);
   if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb, a_mn, b_mn))
     return fail(FP16MC_EINVAL, "a %s tile of lda=%lld / ldb=%lld rows spans 2^32 bytes or more",
-                fp16mc::gemm_plan_name(plan), (long long)lda, (long long)ldb);
+                fp16mc::gemm_plan_name(plan, a_mn, b_mn), (long long)lda, (long long)ldb);
   fp16mc::GemmProblem p{A,      B,       Out,     M,       N,       K,
                         lda,    ldb,     ldo,     batch,   strideA, strideB,
                         strideO, static_cast<fp16mc::Dtype>(ab_type), static_cast<fp16mc::Dtype>(out_type),
@@ -149,12 +149,12 @@ int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_ma
 }
 
 const char* gemm_nt_f16f32_plan(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, false, false));
+  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, false, false), false, false);
 }
 
 const char* gemm_ex_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int a_order, int b_order) {
-  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, a_order == FP16MC_MN_CONTIGUOUS,
-                                                         b_order == FP16MC_MN_CONTIGUOUS));
+  const bool a_mn = a_order == FP16MC_MN_CONTIGUOUS, b_mn = b_order == FP16MC_MN_CONTIGUOUS;
+  return fp16mc::gemm_plan_name(fp16mc::choose_gemm_plan(M, N, K, batch, a_mn, b_mn), a_mn, b_mn);
 }
 
 const char* fp16mc_last_error(void) { return g_err; }

@@ -19,14 +19,13 @@
 //                   row fetch one whole 128-byte line, which halves the L2
 //                   requests of BK = 32 (two half-line requests per line).
 //   LDS -> VGPR     one ds_read_b128 per lane per operand fragment: the 8
-//                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 takes
-//                   from each lane.  Both operands are K-contiguous (NT), so
-//                   no transpose is needed.
+//                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 (or
+//                   v_mfma_f32_16x16x32_f16) takes from each lane.  Both
+//                   operands are K-contiguous (NT), so no transpose is needed.
 //   MFMA            A's fragment is the instruction's first operand, B's
-//                   the second, so in each accumulator register the 32
-//                   lanes of a half-wavefront hold 32 consecutive columns of
-//                   one output row: a dword store per register writes two
-//                   whole 128-byte row segments.
+//                   the second, so in each accumulator register consecutive
+//                   lanes hold consecutive columns of one output row (32 for
+//                   32x32 tiles, 16 for 16x16 ones).
 //   K loop          a ring of LDS stages; each slice's loads are issued
 //                   STAGES-1 slices ahead, spread between MFMAs, and the
 //                   fragments of the next K step are read while the current
@@ -54,21 +53,58 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Operand element types.  Both move through the kernels as raw 16-bit
 // patterns; only the matrix instruction that consumes them differs.
+// The accumulator type picks the instruction shape: 32x32x16 or 16x16x32.
 struct InF16 {
   typedef f16x8 V8;
-  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+  static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 struct InBF16 {
   typedef bf16x8 V8;
-  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+  static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Lane maps of the two instruction shapes as the kernel uses them: the
+// operand row and 8-wide K group of a lane (a K step of kK values is
+// kGroups groups), its accumulator cells, and for transposed tiles the K
+// row and M offset of the 8 bytes it names in a ds_read_b64_tr_b16.
+template <int MI>
+struct Mma;
+template <>
+struct Mma<32> {
+  static constexpr int kM = mfma32::kM, kK = mfma32::kK, kAcc = mfma32::kAcc, kGroups = 2;
+  typedef f32x16 Acc;
+  static __device__ __forceinline__ int row(int lane) { return mfma32::operand_row(lane); }
+  static __device__ __forceinline__ int kgroup(int lane) { return lane >> 5; }
+  static __device__ __forceinline__ int acc_row(int lane, int v) { return mfma32::acc_row(lane, v); }
+  static __device__ __forceinline__ int acc_col(int lane) { return mfma32::acc_col(lane, 0); }
+  static __device__ __forceinline__ int tr_k(int lane) { return 8 * (lane >> 5) + ((lane >> 2) & 3); }
+  static __device__ __forceinline__ int tr_m(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+};
+template <>
+struct Mma<16> {
+  static constexpr int kM = mfma16::kM, kK = mfma16::kK, kAcc = mfma16::kAcc, kGroups = 4;
+  typedef f32x4 Acc;
+  static __device__ __forceinline__ int row(int lane) { return mfma16::operand_row(lane); }
+  static __device__ __forceinline__ int kgroup(int lane) { return lane >> 4; }
+  static __device__ __forceinline__ int acc_row(int lane, int v) { return mfma16::acc_row(lane, v); }
+  static __device__ __forceinline__ int acc_col(int lane) { return mfma16::acc_col(lane, 0); }
+  static __device__ __forceinline__ int tr_k(int lane) { return 8 * (lane >> 4) + ((lane >> 2) & 3); }
+  static __device__ __forceinline__ int tr_m(int lane) { return 4 * (lane & 3); }
 };
 
 // One output element: the fp32 sum, plus the element's previous value when
@@ -80,12 +116,12 @@ __device__ __forceinline__ void store_out(OutT* p, float v) {
 }
 
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
-// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in slices
-// of BK (32 or 64) held in a ring of STAGES LDS stages; WAVES_PER_SIMD
-// workgroups' worth of wavefronts share each SIMD (the register budget
-// follows from it).
+// (BM/WM) x (BN/WN) sub-tile made of MI x MI MFMA tiles (MI = 32: 32x32x16,
+// MI = 16: 16x16x32).  K advances in slices of BK (32 or 64) held in a ring
+// of STAGES LDS stages; WAVES_PER_SIMD workgroups' worth of wavefronts share
+// each SIMD (the register budget follows from it).
 template <int BM_, int BN_, int WM_, int WN_, int GROUP_M_, int STAGES_, int WAVES_PER_SIMD_, int BK_ = 32,
-          int STREAM_ = 0>
+          int STREAM_ = 0, int MI_ = 32>
 struct Cfg {
   // STREAM bit 0 / bit 1: A's / B's tiles are read by one workgroup only, so
   // their direct loads are non-temporal (no reuse to keep them cached for).
@@ -93,12 +129,14 @@ struct Cfg {
   static constexpr int STREAM = STREAM_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GROUP_M = GROUP_M_;
   static constexpr int BK = BK_;
+  static constexpr int MI = MI_;
+  using Mm = Mma<MI_>;
   using Swz = LdsSwizzle<2 * BK_>;
   static constexpr int STAGES = STAGES_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int SI = WTM / 32, SJ = WTN / 32;
+  static constexpr int SI = WTM / MI, SJ = WTN / MI;
   static constexpr int A_STAGE = BM * Swz::kRowBytes;
   static constexpr int B_STAGE = BN * Swz::kRowBytes;
   static constexpr int ROWS_PER_WAVE = 1024 / Swz::kRowBytes;     // one 1 KiB direct load
@@ -107,7 +145,8 @@ struct Cfg {
   static constexpr int B_LOADS = BN / ROWS_PER_PASS;
   static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
   static_assert(BK == 32 || BK == 64, "an LDS row holds one 32- or 64-wide K slice");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+  static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be whole MFMA tiles");
+  static_assert(BK % (2 * Mm::kK) == 0, "a slice holds an even number of K steps");
   static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "rows must split evenly");
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   static constexpr int WGS_PER_CU = WAVES_PER_SIMD * 256 / NT > 0 ? WAVES_PER_SIMD * 256 / NT : 1;
@@ -123,7 +162,14 @@ using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // Every CU finishes its tile at the same moment, so each wave of tiles ends
 // in one HBM-bound burst of output writes (about 6% of the 8192^3 time);
 // non-temporal stores shorten it by about a third.
-using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
+// 16x16x32 instructions: with random operands the chip is power-bound, and
+// the 16x16 form sustains about 17% more MFMA throughput than the 32x32 one
+// (it moves half the accumulator per flop); 8192^3 is 5-8% faster with it.
+// The smaller tile shapes measured neutral or slower with it, and so do
+// operands stored MN-contiguous (their per-fragment LDS offsets no longer fit
+// beside two 16x16 fragment sets: NN and TN spilled), which keep 32x32x16.
+using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
+using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
 // Tall 64x32 tiles for N <= 32: the product streams A (read by one
 // workgroup each, non-temporal) against a B that every workgroup shares.
 // 16384x8x16384: 93 us against 118 us for a dedicated register-streaming
@@ -191,6 +237,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
+
+// The K loop's lambdas hold the accumulators and fragments by reference:
+// they must be inlined for those arrays to live in registers.
+#define FP16MC_INLINE __attribute__((always_inline))
 
 // Scheduling hints: keep `n` instructions of one kind together at this point.
 #define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
@@ -292,7 +342,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         off[p] = static_cast<unsigned>(2 * (rr * ld + 8 * C::Swz::logical_chunk(r, pchunk)));
       }
     } else {
-      using TZ = TrSwizzle<2 * decltype(w)::value>;
+      using TZ = TrSwizzle<2 * decltype(w)::value, C::MI>;
       constexpr int RK = 1024 / TZ::kRowBytes;     // K rows per 1 KiB span
       const int kr = lane / TZ::kChunks;
       const int pc = lane % TZ::kChunks;
@@ -324,7 +374,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   constexpr int kLoads = C::A_LOADS + C::B_LOADS;   // direct loads per slice per wavefront
   constexpr bool kNtA = (C::STREAM & 1) != 0, kNtB = (C::STREAM & 2) != 0;
   // All direct loads of slice `slice` (A's, then B's).
-  auto dma_all = [&](unsigned char* as, unsigned char* bs, int64_t slice) {
+  auto dma_all = [&](unsigned char* as, unsigned char* bs, int64_t slice) FP16MC_INLINE {
     const unsigned koff = static_cast<unsigned>(2 * C::BK * slice);
     if constexpr (!A_MN) {
 #pragma unroll
@@ -343,9 +393,22 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       for (int q = 0; q < C::B_LOADS; ++q) dma16<kNtB>(r, bs + span(q), b_off[q], 0);
     }
   };
+  // Direct load q (A's first, then B's) of slice `slice`.
+  auto dma_one = [&](unsigned char* as, unsigned char* bs, int64_t slice, auto qc) FP16MC_INLINE {
+    constexpr int q = decltype(qc)::value;
+    const unsigned koff = static_cast<unsigned>(2 * C::BK * slice);
+    if constexpr (q < C::A_LOADS) {
+      if constexpr (!A_MN) dma16<kNtA>(a_rsrc, as + span(q), a_off[q], koff);
+      else dma16<kNtA>(slice_rsrc(a_tile, lda, M - i0, slice), as + span(q), a_off[q], 0);
+    } else {
+      constexpr int qb = q - C::A_LOADS;
+      if constexpr (!B_MN) dma16<kNtB>(b_rsrc, bs + span(qb), b_off[qb], koff);
+      else dma16<kNtB>(slice_rsrc(b_tile, ldb, N - j0, slice), bs + span(qb), b_off[qb], 0);
+    }
+  };
   // Last, partial K slice (index nfull): K-contiguous operands through
   // registers with per-element masks, MN-contiguous ones by direct loads.
-  auto load_tail = [&](unsigned char* as, unsigned char* bs, int64_t slice) {
+  auto load_tail = [&](unsigned char* as, unsigned char* bs, int64_t slice) FP16MC_INLINE {
     const int64_t k0 = slice * C::BK;
     if constexpr (!A_MN) {
 #pragma unroll
@@ -376,18 +439,19 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   };
 
   // ---- fragment reads + MFMA ------------------------------------------------
-  f32x16 acc[C::SI][C::SJ];
+  using Mm = typename C::Mm;
+  typename Mm::Acc acc[C::SI][C::SJ];
 #pragma unroll
   for (int si = 0; si < C::SI; ++si)
 #pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj) acc[si][sj] = f32x16{};
+    for (int sj = 0; sj < C::SJ; ++sj) acc[si][sj] = typename Mm::Acc{};
 
-  const int frow = mfma32::operand_row(lane);      // row inside a 32-row MFMA tile
-  const int khalf = lane >> 5;                     // which 8-wide K group of a 16-K step
+  const int frow = Mm::row(lane);                  // row inside an MFMA tile
+  const int kgrp = Mm::kgroup(lane);               // which 8-wide K group of a K step
   const int key = C::Swz::key(frow);          // equal to key(row) for every fragment row
   const int a_row0 = (wm * C::WTM + frow) * C::Swz::kRowBytes;
   const int b_row0 = (wn * C::WTN + frow) * C::Swz::kRowBytes;
-  constexpr int KK = C::BK / mfma32::kK;           // 16-wide K steps per slice (2 or 4)
+  constexpr int KK = C::BK / Mm::kK;               // K steps per slice (2 or 4)
   constexpr int NMF = C::SI * C::SJ;               // MFMAs per K step
   // LDS reads per K step: one ds_read_b128 per K-contiguous fragment, two
   // ds_read_b64_tr_b16 per MN-contiguous one.
@@ -398,54 +462,54 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     typename In::V8 a[C::SI];
     typename In::V8 b[C::SJ];
   };
-  // MN-contiguous tiles: lane l = 16g + 4r + q reads K row 8(l/32) + r (+4 for
-  // the second half, +16 kk) at m = 16(g%2) + 4q of each 32-wide MFMA tile;
-  // the swizzle key is a per-lane constant (it uses K-row bits 0, 1 and 3).
+  // MN-contiguous tiles: lane l = 16g + 4r + q names K row Mm::tr_k(l) (+4
+  // for the second half of its 8 K values, +kK per K step) at M offset
+  // Mm::tr_m(l) of each MFMA tile; the swizzle key is a per-lane constant.
   int a_tr[C::SI];
   int b_tr[C::SJ];
   if constexpr (A_MN) {
-    using TZ = TrSwizzle<2 * C::BM>;
-    const int kr = 8 * khalf + ((lane >> 2) & 3);
-    const int mo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    using TZ = TrSwizzle<2 * C::BM, C::MI>;
 #pragma unroll
-    for (int si = 0; si < C::SI; ++si) a_tr[si] = TZ::offset_bytes(kr, wm * C::WTM + 32 * si + mo);
+    for (int si = 0; si < C::SI; ++si)
+      a_tr[si] = TZ::offset_bytes(Mm::tr_k(lane), wm * C::WTM + Mm::kM * si + Mm::tr_m(lane));
   }
   if constexpr (B_MN) {
-    using TZ = TrSwizzle<2 * C::BN>;
-    const int kr = 8 * khalf + ((lane >> 2) & 3);
-    const int mo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    using TZ = TrSwizzle<2 * C::BN, C::MI>;
 #pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj) b_tr[sj] = TZ::offset_bytes(kr, wn * C::WTN + 32 * sj + mo);
+    for (int sj = 0; sj < C::SJ; ++sj)
+      b_tr[sj] = TZ::offset_bytes(Mm::tr_k(lane), wn * C::WTN + Mm::kM * sj + Mm::tr_m(lane));
   }
-  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) {
-    const int pc = ((2 * kk + khalf) ^ key) << 4;
-#pragma unroll
-    for (int si = 0; si < C::SI; ++si) {
+  // Fragment x of K step kk: A's fragment si = x for x < SI, else B's sj = x - SI.
+  auto read_one = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f, auto xc) FP16MC_INLINE {
+    constexpr int x = decltype(xc)::value;
+    static_assert(x >= 0 && x < C::SI + C::SJ, "fragment index");
+    const int pc = ((Mm::kGroups * kk + kgrp) ^ key) << 4;
+    if constexpr (x < C::SI) {
+      constexpr int si = x;
       if constexpr (!A_MN) {
-        f.a[si] = *reinterpret_cast<const typename In::V8*>(as + a_row0 + si * 32 * C::Swz::kRowBytes + pc);
+        f.a[si] = *reinterpret_cast<const typename In::V8*>(as + a_row0 + si * Mm::kM * C::Swz::kRowBytes + pc);
       } else {
-        const unsigned char* p = as + a_tr[si] + 16 * kk * (2 * C::BM);
+        const unsigned char* p = as + a_tr[si] + Mm::kK * kk * (2 * C::BM);
         f.a[si] = tr_read8<typename In::V8>(p, p + 4 * (2 * C::BM));
       }
-    }
-#pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj) {
+    } else {
+      constexpr int sj = x - C::SI;
       if constexpr (!B_MN) {
-        f.b[sj] = *reinterpret_cast<const typename In::V8*>(bs + b_row0 + sj * 32 * C::Swz::kRowBytes + pc);
+        f.b[sj] = *reinterpret_cast<const typename In::V8*>(bs + b_row0 + sj * Mm::kM * C::Swz::kRowBytes + pc);
       } else {
-        const unsigned char* p = bs + b_tr[sj] + 16 * kk * (2 * C::BN);
+        const unsigned char* p = bs + b_tr[sj] + Mm::kK * kk * (2 * C::BN);
         f.b[sj] = tr_read8<typename In::V8>(p, p + 4 * (2 * C::BN));
       }
     }
   };
-  auto mfma = [&](const Frags& f, int n) {
+  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) FP16MC_INLINE {
+    static_for<C::SI + C::SJ>([&](auto x) { read_one(as, bs, kk, f, x); });
+  };
+  auto mfma = [&](const Frags& f, int n) FP16MC_INLINE {
     const int si = n / C::SJ, sj = n % C::SJ;
-    acc[si][sj] = In::mfma32(f.a[si], f.b[sj], acc[si][sj]);
+    acc[si][sj] = In::mma(f.a[si], f.b[sj], acc[si][sj]);
   };
-  auto mfma_all = [&](const Frags& f) {
-#pragma unroll
-    for (int n = 0; n < NMF; ++n) mfma(f, n);
-  };
+  auto mfma_all = [&](const Frags& f) FP16MC_INLINE { static_for<NMF>([&](auto n) { mfma(f, decltype(n)::value); }); };
   // Wait until at most `n` direct loads of this thread are in flight and its
   // LDS reads/writes are done, then make everyone's writes visible.
   // (A plain s_barrier: a fenced __syncthreads would also wait for the loads
@@ -478,7 +542,20 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   };
   std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
   constexpr int kLoadSteps = 2;                    // MFMA steps the slice loads are spread over
-  auto phase = [&](auto st, int64_t s, auto pending) {
+  // With 16x16 tiles a fragment set is 64 VGPRs, and the scheduler's own
+  // interleaving (or group hints) keeps a third set live and shuffles the
+  // accumulators.  Those phases are issued in a fixed order instead, fenced
+  // in small groups: step 0's reads, then the carried MFMAs with a slice load
+  // after every kLdEvery-th; then each later step's MFMAs with the next
+  // step's fragment reads after every kRdEvery-th, so that the last read has
+  // a quarter of the step to land before the barrier.
+  constexpr bool kPinned = C::MI == 16;
+  constexpr int kLdEvery = NMF / kLoads > 0 ? NMF / kLoads : 1;
+  constexpr int kFrags = C::SI + C::SJ;            // fragments per K step (read_one calls)
+  constexpr int kRdEvery = NMF / kFrags > 1 ? NMF / kFrags * 3 / 4 : 1;
+  static_assert(!kPinned || (kLdEvery * (kLoads - 1) < KK * NMF && kRdEvery * (kFrags - 1) < NMF),
+                "every load and read finds an MFMA to follow");
+  auto phase = [&](auto st, int64_t s, auto pending) FP16MC_INLINE {
     constexpr int S = decltype(st)::value;
     constexpr bool kPending = decltype(pending)::value;
     unsigned char* as = stage_a(st);
@@ -486,6 +563,39 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     unsigned char* an = stage_a(std::integral_constant<int, S + kAhead>{});
     unsigned char* bn = stage_b(std::integral_constant<int, S + kAhead>{});
     const int64_t next = slice_of(s + kAhead);
+    if constexpr (kPinned) {
+      read_frags(as, bs, 0, f0);
+      sched_fence();
+      if constexpr (kPending) {
+        static_for<NMF>([&](auto n) {
+          constexpr int i = decltype(n)::value;
+          mfma(f1, i);
+          if constexpr (i % kLdEvery == 0 && i / kLdEvery < kLoads)
+            dma_one(an, bn, next, std::integral_constant<int, i / kLdEvery>{});
+          sched_fence();
+        });
+      } else {
+        dma_all(an, bn, next);
+        sched_fence();
+      }
+      static_for<KK - 1>([&](auto t) {
+        constexpr int kk = decltype(t)::value + 1;
+        Frags& cur = kk % 2 == 1 ? f0 : f1;
+        Frags& nxt = kk % 2 == 1 ? f1 : f0;
+        static_for<NMF>([&](auto n) {
+          constexpr int i = decltype(n)::value;
+          constexpr int g = kk * NMF + i;          // MFMA index in the phase
+          mfma(cur, i);
+          if constexpr (kPending && g % kLdEvery == 0 && g / kLdEvery < kLoads)
+            dma_one(an, bn, next, std::integral_constant<int, g / kLdEvery>{});
+          if constexpr (i % kRdEvery == 0 && i / kRdEvery < kFrags)
+            read_one(as, bs, kk, nxt, std::integral_constant<int, i / kRdEvery>{});
+          sched_fence();
+        });
+      });
+      publish_keep(keep_later);
+      return;
+    }
     read_frags(as, bs, 0, f0);
     if constexpr (kPending) mfma_all(f1);
     dma_all(an, bn, next);
@@ -585,31 +695,32 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   }
 
   // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
-  // i = i0 + wm*WTM + 32 si + 8(v/4) + 4(l/32) + v%4, j = j0 + wn*WTN + 32 sj + l%32:
-  // one dword store per v writes two whole 128-byte row segments.  When
-  // accumulating, a row block's previous values are all loaded before any of
-  // its stores (ldo is a run-time value, so the compiler cannot prove that a
-  // store does not alias a later load and would otherwise wait on each load).
+  // i = i0 + wm*WTM + MI si + acc_row(l, v), j = j0 + wn*WTN + MI sj + acc_col(l):
+  // with 32x32 tiles one dword store per v writes two whole 128-byte row
+  // segments, with 16x16 tiles four 64-byte ones.  When accumulating, a row
+  // block's previous values are all loaded before any of its stores (ldo is
+  // a run-time value, so the compiler cannot prove that a store does not
+  // alias a later load and would otherwise wait on each load).
 #pragma unroll
   for (int si = 0; si < C::SI; ++si) {
-    float prev[C::SJ][16];
+    float prev[C::SJ][Mm::kAcc];
     if constexpr (ACC) {
 #pragma unroll
       for (int sj = 0; sj < C::SJ; ++sj) {
-        const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
+        const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+        for (int v = 0; v < Mm::kAcc; ++v) {
+          const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
           prev[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
         }
       }
     }
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj) {
-      const int64_t j = j0 + wn * C::WTN + sj * 32 + mfma32::acc_col(lane, 0);
+      const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + wm * C::WTM + si * 32 + mfma32::acc_row(lane, v);
+      for (int v = 0; v < Mm::kAcc; ++v) {
+        const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
         const float val = ACC ? acc[si][sj][v] + prev[sj][v] : acc[si][sj][v];
         if (i < M && j < N) {
           if constexpr ((C::STREAM & 4) != 0) __builtin_nontemporal_store(static_cast<OutT>(val), Out + i * ldo + j);
@@ -680,7 +791,9 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
   switch (plan) {
     case GemmPlan::kWave32: return launch_cfg<CfgWave32, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64: return launch_cfg<CfgWg128x64, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg256: return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256:
+      if constexpr (A_MN || B_MN) return launch_cfg<CfgWg256Mn, A_MN, B_MN>(p, stream);
+      else return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
     case GemmPlan::kTall: return launch_cfg<CfgTall, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64Stream: return launch_cfg<CfgWg128x64Stream, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg256x128: return launch_cfg<CfgWg256x128, A_MN, B_MN>(p, stream);

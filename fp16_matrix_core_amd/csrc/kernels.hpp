@@ -43,7 +43,9 @@ enum class GemmPlan : int {
 };
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool a_mn, bool b_mn);
-const char* gemm_plan_name(GemmPlan plan);
+// The plan's kernel name for one storage order of the operands (a_mn / b_mn:
+// A / B stored with M / N contiguous).
+const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn);
 // Number of workgroups the plan launches (host-side; used to validate the grid).
 int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch);
 hipError_t launch_gemm(GemmPlan plan, const GemmProblem& p, hipStream_t stream);

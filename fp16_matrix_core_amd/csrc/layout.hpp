@@ -5,6 +5,7 @@
 //                 rows that hold a 32- or 64-element fp16 K slice of an
 //                 operand tile.
 //   mfma32        lane maps of v_mfma_f32_32x32x16_f16.
+//   mfma16        lane maps of v_mfma_f32_16x16x32_f16.
 //   m8n8          the 8x8 b16 matrix fragment of the warp-collective matrix
 //                 load/store, mapped onto 64-lane wavefronts.
 //
@@ -32,9 +33,11 @@ namespace fp16mc {
 // served 16 lanes at a time, the four groups being the lanes with equal
 // (bit 5, bit 4 ^ bit 2) of the lane id -- e.g. lanes {0-3, 8-11, 20-23,
 // 28-31}.  Within a group no two lanes may touch the same bank.  Both keys
-// make the fragment reads (lane l reads row l%32, chunk 2kk + l/32)
-// conflict-free; the direct loads write whole rows as one contiguous
-// kilobyte per wavefront (lane l at byte 16 l), which never conflicts.
+// make the 32x32x16 fragment reads (lane l reads row l%32, chunk
+// 2kk + l/32) conflict-free, and the 128-byte key the 16x16x32 ones (row
+// l%16, chunk 4kk + l/16); the direct loads write whole rows as one
+// contiguous kilobyte per wavefront (lane l at byte 16 l), which never
+// conflicts.
 // The XOR keeps the map a bijection inside each row.
 // ---------------------------------------------------------------------------
 template <int RowBytes>
@@ -72,30 +75,37 @@ struct LdsSwizzle : RowSwizzle<RowBytes> {
 // M, which ds_read_b64_tr_b16 delivers: in each 16-lane group, lane 4r + q
 // names 8 bytes (4 values) of "row" r of a 4 x 16 block and lane i receives
 // column i of that block (measured on gfx950).  Lane l = 16 g + 4 r + q of a
-// fragment read takes LDS row k0 + r with k0 = 8 (l / 32) (+4 for the
-// second half of the 8 K values) and the 4 values at m = 16 (g % 2) + 4 q.
+// 32x32x16 fragment read takes LDS row k0 + r with k0 = 8 (l / 32) (+4 for
+// the second half of the 8 K values) and the 4 values at m = 16 (g % 2) + 4 q;
+// of a 16x16x32 one, row 8 g + r (+4) and the values at m = 4 q.
 //
 // Chunk c of row k is stored at physical chunk c ^ key(k), with
-//   64-byte rows    key = 2 ((k >> 3) & 1)
-//   128-byte rows   key = 4 ((k >> 1) & 1) + 2 ((k >> 3) & 1)
-//   >= 256 bytes    key = 4 (k & 3) + 2 ((k >> 3) & 1)   (low 4 chunk bits)
-// so that the 32 lanes served together -- lanes [0, 32) and [32, 64), or
-// lanes with equal bit 4 -- touch 64 distinct banks (tests/host simulates
-// both pairings).  The key uses only bits 0, 1 and 3 of k, i.e. it is a
-// per-lane constant of a fragment read.  Direct loads fill whole rows as
-// contiguous 1 KiB spans, as for K-contiguous tiles.
+//   64-byte rows    key = 2 b
+//   128-byte rows   key = 4 ((k >> 1) & 1) + 2 b
+//   >= 256 bytes    key = 4 (k & 3) + 2 b   (low 4 chunk bits)
+// where b = bit 3 of k for 32x32x16 fragments and bit 3 ^ bit 4 of k for
+// 16x16x32 ones (MI = 16: lane l = 16 g + 4 r + q reads K row 8 g + r, so
+// the lanes of a 32-lane pass differ in K-row bit 3 or bit 4).  The 32 lanes
+// served together -- lanes [0, 32) and [32, 64), or lanes with equal bit 4 --
+// then touch 64 distinct banks (tests/host simulates both pairings).  The
+// key uses only K-row bits that are constant across a fragment's K steps
+// (0, 1 and 3, and 4 for MI = 16), i.e. it is a per-lane constant of a
+// fragment read.  Direct loads fill whole rows as contiguous 1 KiB spans, as
+// for K-contiguous tiles.
 // ---------------------------------------------------------------------------
-template <int RowBytes>
+template <int RowBytes, int MI = 32>
 struct TrSwizzle {
   static_assert(RowBytes == 64 || RowBytes == 128 || (RowBytes >= 256 && RowBytes % 256 == 0),
                 "transposed tiles are 32, 64 or a multiple of 128 values wide");
+  static_assert(MI == 32 || MI == 16, "32x32x16 or 16x16x32 fragments");
   static constexpr int kRowBytes = RowBytes;
   static constexpr int kChunks = RowBytes / 16;
   FP16MC_HD static constexpr int key(int k) {
-    return RowBytes == 64    ? 2 * ((k >> 3) & 1)
-           : RowBytes == 128 ? 4 * ((k >> 1) & 1) + 2 * ((k >> 3) & 1)
-                             : 4 * (k & 3) + 2 * ((k >> 3) & 1);
+    return RowBytes == 64    ? 2 * kbit(k)
+           : RowBytes == 128 ? 4 * ((k >> 1) & 1) + 2 * kbit(k)
+                             : 4 * (k & 3) + 2 * kbit(k);
   }
+  FP16MC_HD static constexpr int kbit(int k) { return MI == 16 ? ((k >> 3) ^ (k >> 4)) & 1 : (k >> 3) & 1; }
   FP16MC_HD static constexpr int phys_chunk(int k, int chunk) { return chunk ^ key(k); }
   FP16MC_HD static constexpr int logical_chunk(int k, int phys) { return phys ^ key(k); }
   // byte offset of element m of row k
@@ -118,6 +128,21 @@ FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 5) + e;
 FP16MC_HD constexpr int acc_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 31; }
 }  // namespace mfma32
+
+// ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x32_f16: D(16x16) += X(16x32) * Y(32x16), the same rate per
+// cycle as the 32x32 form with half the accumulator per instruction.
+// Operands: lane l supplies 8 fp16 of X row (l % 16), and 8 fp16 of Y column
+// (l % 16), both at k = 8*(l / 16) + e, e in [0, 8).
+// Accumulator: 4 fp32 per lane; element v of lane l is D[4*(l/16) + v][l % 16].
+// ---------------------------------------------------------------------------
+namespace mfma16 {
+constexpr int kM = 16, kN = 16, kK = 32, kAcc = 4;
+FP16MC_HD constexpr int operand_row(int lane) { return lane & 15; }
+FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 4) + e; }
+FP16MC_HD constexpr int acc_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 15; }
+}  // namespace mfma16
 
 // ---------------------------------------------------------------------------
 // m8n8 fragment of the matrix load/store: over a 32-lane group, lane l holds

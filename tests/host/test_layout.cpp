@@ -67,6 +67,16 @@ void check_swizzle() {
       CHECK(b128_conflicts(addr) == 0, "fragment-read bank conflict base %d kk %d (%d-byte rows)", base, kk,
             RowBytes);
     }
+  // 16x16x32 fragment reads (128-byte rows, i.e. 64-wide K slices): lane l
+  // reads row base + l%16, logical chunk 4kk + l/16.
+  if (RowBytes == 128)
+    for (int base = 0; base < 256; base += 16)
+      for (int kk = 0; kk < kc / 4; ++kk) {
+        int addr[64];
+        for (int l = 0; l < 64; ++l) addr[l] = Z::offset_bytes(base + (l & 15), 4 * kk + (l >> 4));
+        CHECK(b128_conflicts(addr) == 0, "16x16 fragment-read bank conflict base %d kk %d", base, kk);
+        CHECK(Z::key(base) == Z::key(0), "key differs between 16-row MFMA tiles");
+      }
   // direct loads: one wavefront writes 1 KiB = 1024/RowBytes whole rows contiguously
   const int rows = 1024 / RowBytes;
   for (int r0 = 0; r0 < 256; r0 += rows) {
@@ -106,9 +116,9 @@ static bool b64_conflict_free(const int (&addr)[64], int pairing) {
 
 // Transposed tiles: bijective rows, whole-row direct loads, fragment reads that
 // deliver the MFMA operand map, conflict-free under both pass pairings.
-template <int RowBytes>
+template <int RowBytes, int MI = 32>
 void check_tr_swizzle(int bk) {
-  using Z = TrSwizzle<RowBytes>;
+  using Z = TrSwizzle<RowBytes, MI>;
   const int W = RowBytes / 2;   // values per row
   for (int k = 0; k < 64; ++k) {
     std::set<int> seen;
@@ -132,6 +142,30 @@ void check_tr_swizzle(int bk) {
   std::vector<int> img(bk * W);
   for (int k = 0; k < bk; ++k)
     for (int m = 0; m < W; ++m) img[Z::offset_bytes(k, m) / 2] = k * 1000 + m;
+  if (MI == 16) {
+    // 16x16x32: lane l = 16 g + 4 r + q reads K row 32 kk + 8 g + 4 t + r, values m = mbase + 4 q
+    for (int kk = 0; kk < bk / 32; ++kk)
+      for (int t = 0; t < 2; ++t)
+        for (int mbase = 0; mbase < W; mbase += 16) {
+          int addr[64];
+          for (int l = 0; l < 64; ++l) {
+            const int k = 32 * kk + 8 * (l >> 4) + 4 * t + ((l >> 2) & 3);
+            addr[l] = Z::offset_bytes(k, mbase + 4 * (l & 3));
+          }
+          int got[64][4];
+          tr16_read(img, addr, got);
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 4; ++e) {
+              const int k = 32 * kk + mfma16::operand_k(l, 4 * t + e), m = mbase + mfma16::operand_row(l);
+              CHECK(got[l][e] == k * 1000 + m, "tr16 fragment wrong: rows %d, lane %d, e %d", RowBytes, l, e);
+            }
+          CHECK(b64_conflict_free(addr, 0), "tr16 read conflicts (pairing 0, %d-byte rows, kk %d t %d m %d)",
+                RowBytes, kk, t, mbase);
+          CHECK(b64_conflict_free(addr, 1), "tr16 read conflicts (pairing 1, %d-byte rows, kk %d t %d m %d)",
+                RowBytes, kk, t, mbase);
+        }
+    return;
+  }
   for (int kk = 0; kk < bk / 16; ++kk)
     for (int t = 0; t < 2; ++t)
       for (int mbase = 0; mbase < W; mbase += 32) {
@@ -169,6 +203,16 @@ int main() {
   check_tr_swizzle<128>(64);
   check_tr_swizzle<256>(64);
   check_tr_swizzle<512>(64);
+  check_tr_swizzle<128, 16>(64);
+  check_tr_swizzle<256, 16>(64);
+  check_tr_swizzle<512, 16>(64);
+  // the 32x32x16 key would conflict for 16x16x32 reads under the bit-4 pairing
+  {
+    using Z = TrSwizzle<512, 32>;
+    int addr[64];
+    for (int l = 0; l < 64; ++l) addr[l] = Z::offset_bytes(8 * (l >> 4) + ((l >> 2) & 3), 4 * (l & 3));
+    CHECK(!b64_conflict_free(addr, 1), "32x32 tr key should conflict for 16x16 reads");
+  }
   // the model reproduces the measured conflicts of unswizzled rows
   {
     int addr[64];
@@ -193,6 +237,13 @@ int main() {
     for (int l = 0; l < 64; ++l)
       for (int e = 0; e < 8; ++e) ops.insert({mfma32::operand_row(l), mfma32::operand_k(l, e)});
     CHECK(ops.size() == 32 * 16, "mfma32 operand map not a bijection");
+    std::set<std::pair<int, int>> cells16, ops16;
+    for (int l = 0; l < 64; ++l)
+      for (int v = 0; v < mfma16::kAcc; ++v) cells16.insert({mfma16::acc_row(l, v), mfma16::acc_col(l, v)});
+    CHECK(cells16.size() == 16 * 16, "mfma16 accumulator map not a bijection");
+    for (int l = 0; l < 64; ++l)
+      for (int e = 0; e < 8; ++e) ops16.insert({mfma16::operand_row(l), mfma16::operand_k(l, e)});
+    CHECK(ops16.size() == 16 * 32, "mfma16 operand map not a bijection");
   }
   // m8n8: each 32-lane half covers the 8 rows x 4 column pairs once; images are bijections
   for (int num : {1, 2, 4})

@@ -143,6 +143,11 @@ def test_plans_by_storage_order(L):
         assert f.plan_ex(100, 40, 64, 1, *order).startswith("wg128x64_")
         assert f.plan_ex(16, 8, 16, 1, *order).startswith("wave32x32")
         assert f.plan_ex(8192, 8192, 8192, 1, *order).startswith("wg256x256")
+    # 256x256 tiles use 16x16x32 instructions for K-contiguous operands, 32x32x16 otherwise
+    assert f.plan_ex(8192, 8192, 8192, 1, 0, 0) == "wg256x256_w4_mfma16x16x32"
+    assert f.plan(8192, 8192, 8192) == "wg256x256_w4_mfma16x16x32"
+    for order in ((1, 0), (0, 1), (1, 1)):
+        assert f.plan_ex(8192, 8192, 8192, 1, *order) == "wg256x256_w4_mfma32x32x16"
 
 
 def test_gemm_ex_empty_problems(L):
