@@ -242,6 +242,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // they must be inlined for those arrays to live in registers.
 #define FP16MC_INLINE __attribute__((always_inline))
 
+// v_permlane16_swap_b32 x, y: 16-lane rows 1 and 3 of x trade places with
+// rows 0 and 2 of y (measured on gfx950).  Inline assembly: the compiler's
+// builtin for it merged the swaps of different elements of one accumulator
+// vector into one.  The s_nop covers the VALU write of x and y just before.
+__device__ __forceinline__ void permlane16_swap(float& x, float& y) {
+  asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
 // Scheduling hints: keep `n` instructions of one kind together at this point.
 #define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
 #define SCHED_VMEM_READ(n) __builtin_amdgcn_sched_group_barrier(0x020, (n), 0)
@@ -692,6 +700,64 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       read_frags(as, bs, kk, f0);
       mfma_all(f0);
     }
+  }
+
+  // ---- epilogue, 16x16 tiles: the registers of each pair of horizontally
+  // adjacent tiles (sj = 2p, 2p+1) are regrouped with v_permlane16_swap
+  // (16-lane rows 1 and 3 of the first operand trade places with rows 0
+  // and 2 of the second), so that in register t, element v, lane l holds
+  // Out[i][j] with i = i0 + wm*WTM + 16 si + 4t + v + 8(l/32) and
+  // j = j0 + wn*WTN + 32p + l%32: each store writes two whole 32-column
+  // row pieces (128 bytes of fp32) instead of four 16-column ones.
+  if constexpr (C::MI == 16 && C::SJ % 2 == 0) {
+    constexpr int kP = C::SJ / 2;
+#pragma unroll
+    for (int si = 0; si < C::SI; ++si) {
+      float val[kP][2][4];
+#pragma unroll
+      for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          val[pp][0][v] = acc[si][2 * pp][v];
+          val[pp][1][v] = acc[si][2 * pp + 1][v];
+          permlane16_swap(val[pp][0][v], val[pp][1][v]);
+        }
+      const int64_t ib = i0 + wm * C::WTM + si * 16 + 8 * (lane >> 5);
+      const int64_t jb = j0 + wn * C::WTN + (lane & 31);
+      if constexpr (ACC) {
+        float prev[kP][2][4];
+#pragma unroll
+        for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
+              prev[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
+            }
+#pragma unroll
+        for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) val[pp][t][v] += prev[pp][t][v];
+      }
+#pragma unroll
+      for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
+            if (i < M && j < N) {
+              if constexpr ((C::STREAM & 4) != 0)
+                __builtin_nontemporal_store(static_cast<OutT>(val[pp][t][v]), Out + i * ldo + j);
+              else
+                Out[i * ldo + j] = static_cast<OutT>(val[pp][t][v]);
+            }
+          }
+    }
+    return;
   }
 
   // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
