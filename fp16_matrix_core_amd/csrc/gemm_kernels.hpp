@@ -553,12 +553,15 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // With 16x16 tiles a fragment set is 64 VGPRs, and the scheduler's own
   // interleaving (or group hints) keeps a third set live and shuffles the
   // accumulators.  Those phases are issued in a fixed order instead, fenced
-  // in small groups: step 0's reads, then the carried MFMAs with a slice load
-  // after every kLdEvery-th; then each later step's MFMAs with the next
-  // step's fragment reads after every kRdEvery-th, so that the last read has
-  // a quarter of the step to land before the barrier.
+  // in small groups: each step's MFMAs (the first step's are the carried
+  // ones) with the next step's fragment reads after every kRdEvery-th, so
+  // that the last read has a quarter of the step to land, and the slice
+  // loads after every kLdEvery-th of the first step (offset by kLdFirst).
+  // Reads issued back to back instead stall issue: 16 of them ahead of the
+  // carried MFMAs made that step a third slower.
   constexpr bool kPinned = C::MI == 16;
   constexpr int kLdEvery = NMF / kLoads > 0 ? NMF / kLoads : 1;
+  constexpr int kLdFirst = kLdEvery > 1 ? 1 : 0;
   constexpr int kFrags = C::SI + C::SJ;            // fragments per K step (read_one calls)
   constexpr int kRdEvery = NMF / kFrags > 1 ? NMF / kFrags * 3 / 4 : 1;
   static_assert(!kPinned || (kLdEvery * (kLoads - 1) < KK * NMF && kRdEvery * (kFrags - 1) < NMF),
@@ -572,17 +575,18 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     unsigned char* bn = stage_b(std::integral_constant<int, S + kAhead>{});
     const int64_t next = slice_of(s + kAhead);
     if constexpr (kPinned) {
-      read_frags(as, bs, 0, f0);
-      sched_fence();
       if constexpr (kPending) {
         static_for<NMF>([&](auto n) {
           constexpr int i = decltype(n)::value;
           mfma(f1, i);
-          if constexpr (i % kLdEvery == 0 && i / kLdEvery < kLoads)
+          if constexpr (i % kRdEvery == 0 && i / kRdEvery < kFrags)
+            read_one(as, bs, 0, f0, std::integral_constant<int, i / kRdEvery>{});
+          if constexpr (i % kLdEvery == kLdFirst && i / kLdEvery < kLoads)
             dma_one(an, bn, next, std::integral_constant<int, i / kLdEvery>{});
           sched_fence();
         });
       } else {
+        read_frags(as, bs, 0, f0);
         dma_all(an, bn, next);
         sched_fence();
       }
@@ -594,7 +598,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
           constexpr int i = decltype(n)::value;
           constexpr int g = kk * NMF + i;          // MFMA index in the phase
           mfma(cur, i);
-          if constexpr (kPending && g % kLdEvery == 0 && g / kLdEvery < kLoads)
+          if constexpr (kPending && g % kLdEvery == kLdFirst && g / kLdEvery < kLoads)
             dma_one(an, bn, next, std::integral_constant<int, g / kLdEvery>{});
           if constexpr (i % kRdEvery == 0 && i / kRdEvery < kFrags)
             read_one(as, bs, kk, nxt, std::integral_constant<int, i / kRdEvery>{});
