@@ -131,7 +131,7 @@ struct Cfg {
   static constexpr int BK = BK_;
   static constexpr int MI = MI_;
   using Mm = Mma<MI_>;
-  using Swz = LdsSwizzle<2 * BK_>;
+  using Swz = LdsSwizzle<2 * BK_, MI_>;
   static constexpr int STAGES = STAGES_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int NT = WM * WN * 64;

@@ -26,40 +26,55 @@ namespace fp16mc {
 // 64 bytes (BK = 32, 4 chunks of 16 bytes) or 128 bytes (BK = 64, 8 chunks).
 // Logical chunk c of row r is stored at physical chunk c ^ key(r):
 //   64-byte rows   key(r) = (r >> 2) & 3
-//   128-byte rows  key(r) = (r & 7) ^ ((r >> 3) & 1)
-//
+//   128-byte rows  key(r) = (r & 7) ^ ((r >> 3) & 1)           (32x32x16 reads)
+//                  key(r) = r0 | r3 << 1 | r1 << 2              (16x16x32 reads)
+// with ri = bit i of r.
 // Bank model (measured on gfx950 with collision probes and the SQ bank-
 // conflict counter): LDS has 64 banks of 4 bytes, and a ds_read_b128 is
 // served 16 lanes at a time, the four groups being the lanes with equal
 // (bit 5, bit 4 ^ bit 2) of the lane id -- e.g. lanes {0-3, 8-11, 20-23,
 // 28-31}.  Within a group no two lanes may touch the same bank.  Both keys
 // make the 32x32x16 fragment reads (lane l reads row l%32, chunk
-// 2kk + l/32) conflict-free, and the 128-byte key the 16x16x32 ones (row
-// l%16, chunk 4kk + l/16); the direct loads write whole rows as one
+// 2kk + l/32) conflict-free; the direct loads write whole rows as one
 // contiguous kilobyte per wavefront (lane l at byte 16 l), which never
-// conflicts.
+// conflicts.  That lane grouping does not hold for every pattern: the
+// 16x16x32 reads (row l%16, chunk 4kk + l/16), which it predicts to be
+// conflict-free under the 32x32 key, measured about 4 conflict cycles per
+// read (SQ_LDS_BANK_CONFLICT, in the GEMM and in a probe); the 16x16 key
+// above measured none (as did r0<<0|r3<<1|r1<<2 variants with r0 or r0^r1
+// mixed in), so 16x16 tiles use it.
 // The XOR keeps the map a bijection inside each row.
 // ---------------------------------------------------------------------------
-template <int RowBytes>
+template <int RowBytes, int MI = 32>
 struct RowSwizzle;
 
 template <>
-struct RowSwizzle<64> {
+struct RowSwizzle<64, 32> {
   static constexpr int kRowBytes = 64;
   static constexpr int kChunks = 4;
   FP16MC_HD static constexpr int key(int row) { return (row >> 2) & 3; }
 };
 
 template <>
-struct RowSwizzle<128> {
+struct RowSwizzle<128, 32> {
   static constexpr int kRowBytes = 128;
   static constexpr int kChunks = 8;
   FP16MC_HD static constexpr int key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 };
 
-template <int RowBytes>
-struct LdsSwizzle : RowSwizzle<RowBytes> {
-  using Base = RowSwizzle<RowBytes>;
+template <>
+struct RowSwizzle<128, 16> {
+  static constexpr int kRowBytes = 128;
+  static constexpr int kChunks = 8;
+  FP16MC_HD static constexpr int key(int row) {
+    return (row & 1) | (((row >> 3) & 1) << 1) | (((row >> 1) & 1) << 2);
+  }
+};
+
+// MI: the matrix instruction whose fragments are read (32: 32x32x16, 16: 16x16x32).
+template <int RowBytes, int MI = 32>
+struct LdsSwizzle : RowSwizzle<RowBytes, MI> {
+  using Base = RowSwizzle<RowBytes, MI>;
   FP16MC_HD static constexpr int phys_chunk(int row, int chunk) { return chunk ^ Base::key(row); }
   // inverse map (the XOR is its own inverse): which logical chunk sits at a physical one
   FP16MC_HD static constexpr int logical_chunk(int row, int phys) { return phys ^ Base::key(row); }
