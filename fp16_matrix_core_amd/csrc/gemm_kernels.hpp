@@ -156,7 +156,10 @@ struct Cfg {
 using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
 // 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
 // by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
-using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
+// As for every large-tile configuration below, K-contiguous operands use
+// 16x16x32 instructions and MN-contiguous ones 32x32x16 (the "Mn" twin).
+using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 0, 16>;
+using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
 // 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
 // Every CU finishes its tile at the same moment, so each wave of tiles ends
@@ -165,9 +168,11 @@ using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 16x16x32 instructions: with random operands the chip is power-bound, and
 // the 16x16 form sustains about 17% more MFMA throughput than the 32x32 one
 // (it moves half the accumulator per flop); 8192^3 is 5-8% faster with it.
-// The smaller tile shapes measured neutral or slower with it, and so do
-// operands stored MN-contiguous (their per-fragment LDS offsets no longer fit
-// beside two 16x16 fragment sets: NN and TN spilled), which keep 32x32x16.
+// With the fragment reads interleaved the smaller tiles gain from it too
+// (256x128 and 128x128 5-10%, 128x64 2-3%; only single-slice K = 64 loses,
+// 7%). Operands stored MN-contiguous keep 32x32x16: NN and TN spilled (their
+// per-fragment LDS offsets do not fit beside two 16x16 fragment sets) and
+// TT, which did not, was 13% slower.
 using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
 using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
 // Tall 64x32 tiles for N <= 32: the product streams A (read by one
@@ -184,8 +189,10 @@ using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 2, 2, 64, 7>;
 // Intermediate tiles for problems too small to fill the 256 CUs with
 // 256x256 tiles: 256x128 (three 48 KiB stages) and 128x128 (two 32 KiB
 // stages, two workgroups per CU).
-using CfgWg256x128 = Cfg<256, 128, 2, 2, 4, 3, 1, 64>;
-using CfgWg128x128 = Cfg<128, 128, 2, 2, 8, 2, 2, 64>;
+using CfgWg256x128 = Cfg<256, 128, 2, 2, 4, 3, 1, 64, 0, 16>;
+using CfgWg256x128Mn = Cfg<256, 128, 2, 2, 4, 3, 1, 64>;
+using CfgWg128x128 = Cfg<128, 128, 2, 2, 8, 2, 2, 64, 0, 16>;
+using CfgWg128x128Mn = Cfg<128, 128, 2, 2, 8, 2, 2, 64>;
 // Wide 32x64 tiles for M <= 32: the mirror of the tall tiles, B streamed.
 using CfgWide = Cfg<32, 64, 1, 2, 1, 4, 1, 64, 2>;
 
@@ -855,19 +862,24 @@ int64_t plan_tiles(int64_t M, int64_t N, int64_t batch) {
   return tiles_of<C>(M, N, batch, &tm, &tn);
 }
 
+// The 16x16 configuration for K-contiguous operands, its 32x32 twin otherwise.
+template <class C16, class C32, bool A_MN, bool B_MN>
+hipError_t launch_by_order(const GemmProblem& p, hipStream_t stream) {
+  if constexpr (A_MN || B_MN) return launch_cfg<C32, A_MN, B_MN>(p, stream);
+  else return launch_cfg<C16, A_MN, B_MN>(p, stream);
+}
+
 // Launch of one plan for one storage order of the operands.
 template <bool A_MN, bool B_MN>
 hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream) {
   switch (plan) {
     case GemmPlan::kWave32: return launch_cfg<CfgWave32, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg128x64: return launch_cfg<CfgWg128x64, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg256:
-      if constexpr (A_MN || B_MN) return launch_cfg<CfgWg256Mn, A_MN, B_MN>(p, stream);
-      else return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x64: return launch_by_order<CfgWg128x64, CfgWg128x64Mn, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256: return launch_by_order<CfgWg256, CfgWg256Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kTall: return launch_cfg<CfgTall, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64Stream: return launch_cfg<CfgWg128x64Stream, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg256x128: return launch_cfg<CfgWg256x128, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg128x128: return launch_cfg<CfgWg128x128, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256x128: return launch_by_order<CfgWg256x128, CfgWg256x128Mn, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x128: return launch_by_order<CfgWg128x128, CfgWg128x128Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kWide: return launch_cfg<CfgWide, A_MN, B_MN>(p, stream);
     default: return hipSuccess;
   }

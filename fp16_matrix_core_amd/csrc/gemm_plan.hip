@@ -66,14 +66,15 @@ GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool /
 }
 
 const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn) {
+  const bool mn = a_mn || b_mn;   // large tiles: 16x16x32 for K-contiguous operands, else 32x32x16
   switch (plan) {
     case GemmPlan::kWave32: return "wave32x32_mfma32x32x16";
-    case GemmPlan::kWg128x64: return "wg128x64_w4_mfma32x32x16";
-    case GemmPlan::kWg256: return a_mn || b_mn ? "wg256x256_w4_mfma32x32x16" : "wg256x256_w4_mfma16x16x32";
+    case GemmPlan::kWg128x64: return mn ? "wg128x64_w4_mfma32x32x16" : "wg128x64_w4_mfma16x16x32";
+    case GemmPlan::kWg256: return mn ? "wg256x256_w4_mfma32x32x16" : "wg256x256_w4_mfma16x16x32";
     case GemmPlan::kTall: return "tall64x32_w2_mfma32x32x16";
     case GemmPlan::kWg128x64Stream: return "wg128x64s_w4_mfma32x32x16";
-    case GemmPlan::kWg256x128: return "wg256x128_w4_mfma32x32x16";
-    case GemmPlan::kWg128x128: return "wg128x128_w4_mfma32x32x16";
+    case GemmPlan::kWg256x128: return mn ? "wg256x128_w4_mfma32x32x16" : "wg256x128_w4_mfma16x16x32";
+    case GemmPlan::kWg128x128: return mn ? "wg128x128_w4_mfma32x32x16" : "wg128x128_w4_mfma16x16x32";
     case GemmPlan::kWide: return "wide32x64_w2_mfma32x32x16";
     default: return nullptr;
   }
