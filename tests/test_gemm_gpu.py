@@ -88,7 +88,7 @@ def test_permutation_b_exact(f):
     assert np.array_equal(got, A.astype(np.float32)[:, perm])
 
 
-@pytest.mark.parametrize("M,N,plan", [(4096, 3072, "wg256x256"), (8192, 3072, "wg256x128"),
+@pytest.mark.parametrize("M,N,plan", [(4096, 3072, "wg256x256"), (4096, 5120, "wg256x128"),
                                       (8192, 1024, "wg128x128")])
 def test_permutation_large_tiles_exact(f, M, N, plan):
     """A permutation product on each large-tile configuration: any lane-map mistake permutes the output."""

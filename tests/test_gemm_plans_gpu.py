@@ -29,7 +29,7 @@ PLAN_SHAPES = {
     "wide32x64": (20, 1000, 77),
     "wg128x64": (300, 520, 200),
     "wg128x128": (4100, 2050, 100),
-    "wg256x128": (4000, 4100, 4104),
+    "wg256x128": (1003, 4105, 8200),
     "wg256x256": (8100, 2000, 4100),
 }
 ORDERS = [("k", "k"), ("k", "mn"), ("mn", "k"), ("mn", "mn")]

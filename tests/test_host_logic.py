@@ -145,7 +145,7 @@ def test_plans_by_storage_order(L):
         assert f.plan_ex(8192, 8192, 8192, 1, *order).startswith("wg256x256")
     # large tiles use 16x16x32 instructions for K-contiguous operands, 32x32x16 otherwise
     for shape, name in (((8192, 8192, 8192), "wg256x256_w4"), ((8192, 1024, 8192), "wg256x128_w4"),
-                        ((8192, 8192, 1024), "wg128x128_w4"), ((2048, 2048, 2048), "wg128x64_w4")):
+                        ((6144, 6144, 2048), "wg128x128_w4"), ((2048, 2048, 2048), "wg128x64_w4")):
         assert f.plan_ex(*shape, 1, 0, 0) == name + "_mfma16x16x32"
         assert f.plan(*shape) == name + "_mfma16x16x32"
         for order in ((1, 0), (0, 1), (1, 1)):
@@ -191,7 +191,9 @@ def test_plans(L):
     assert f.plan(129, 64, 64, 4096).startswith("wg128x64_")
     assert f.plan(8192, 8192, 8192).startswith("wg256x256")
     assert f.plan(8192, 1024, 8192).startswith("wg256x128")    # 256x256 tiles would fill half the CUs
-    assert f.plan(8192, 8192, 1024).startswith("wg128x128")    # short K: two workgroups per CU
+    assert f.plan(6144, 6144, 2048).startswith("wg128x128")    # two workgroups per CU
+    assert f.plan(3000, 5000, 704).startswith("wg128x128")
+    assert f.plan(12288, 12288, 1024).startswith("wg256x256")  # many waves of tiles: largest tiles
     assert f.plan(2048, 2048, 2048).startswith("wg128x64_")
     assert f.plan(16384, 64, 4096).startswith("wg128x64_")     # 256-wide tiles would be 3/4 empty
     assert f.plan(8, 16384, 16384).startswith("wide32x64")
