@@ -722,6 +722,25 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // row pieces (128 bytes of fp32) instead of four 16-column ones.
   if constexpr (C::MI == 16 && C::SJ % 2 == 0) {
     constexpr int kP = C::SJ / 2;
+    const int64_t jb = j0 + wn * C::WTN + (lane & 31);
+    auto row_base = [&](int si) { return i0 + wm * C::WTM + si * 16 + 8 * (lane >> 5); };
+    // When accumulating, row block si+1's previous values are loaded before
+    // block si is stored, so that only the first block waits for its loads.
+    // (The rows differ, so the order of these loads and stores is free.)
+    auto load_prev = [&](int si, float (&pv)[kP][2][4]) {
+      const int64_t ib = row_base(si);
+#pragma unroll
+      for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
+            pv[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
+          }
+    };
+    float prev[kP][2][4];
+    if constexpr (ACC) load_prev(0, prev);
 #pragma unroll
     for (int si = 0; si < C::SI; ++si) {
       float val[kP][2][4];
@@ -733,25 +752,15 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
           val[pp][1][v] = acc[si][2 * pp + 1][v];
           permlane16_swap(val[pp][0][v], val[pp][1][v]);
         }
-      const int64_t ib = i0 + wm * C::WTM + si * 16 + 8 * (lane >> 5);
-      const int64_t jb = j0 + wn * C::WTN + (lane & 31);
+      const int64_t ib = row_base(si);
       if constexpr (ACC) {
-        float prev[kP][2][4];
-#pragma unroll
-        for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
-              prev[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
-            }
 #pragma unroll
         for (int pp = 0; pp < kP; ++pp)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int v = 0; v < 4; ++v) val[pp][t][v] += prev[pp][t][v];
+        if (si + 1 < C::SI) load_prev(si + 1, prev);
       }
 #pragma unroll
       for (int pp = 0; pp < kP; ++pp)
@@ -774,23 +783,33 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
   // i = i0 + wm*WTM + MI si + acc_row(l, v), j = j0 + wn*WTN + MI sj + acc_col(l):
   // with 32x32 tiles one dword store per v writes two whole 128-byte row
-  // segments, with 16x16 tiles four 64-byte ones.  When accumulating, a row
-  // block's previous values are all loaded before any of its stores (ldo is
-  // a run-time value, so the compiler cannot prove that a store does not
-  // alias a later load and would otherwise wait on each load).
+  // segments, with 16x16 tiles four 64-byte ones.  When accumulating, the
+  // previous values of row block si+1 are all loaded before any store of
+  // block si (ldo is a run-time value, so the compiler cannot prove that a
+  // store does not alias a later load and would otherwise wait on each
+  // load; one block ahead, only the first block's loads are waited for).
+  auto load_prev = [&](int si, float (&pv)[C::SJ][Mm::kAcc]) {
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj) {
+      const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
+#pragma unroll
+      for (int v = 0; v < Mm::kAcc; ++v) {
+        const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
+        pv[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
+      }
+    }
+  };
+  float prev[2][C::SJ][Mm::kAcc];
+  if constexpr (ACC) load_prev(0, prev[0]);
 #pragma unroll
   for (int si = 0; si < C::SI; ++si) {
-    float prev[C::SJ][Mm::kAcc];
+    float val[C::SJ][Mm::kAcc];
+#pragma unroll
+    for (int sj = 0; sj < C::SJ; ++sj)
+#pragma unroll
+      for (int v = 0; v < Mm::kAcc; ++v) val[sj][v] = ACC ? acc[si][sj][v] + prev[si % 2][sj][v] : acc[si][sj][v];
     if constexpr (ACC) {
-#pragma unroll
-      for (int sj = 0; sj < C::SJ; ++sj) {
-        const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
-#pragma unroll
-        for (int v = 0; v < Mm::kAcc; ++v) {
-          const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
-          prev[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
-        }
-      }
+      if (si + 1 < C::SI) load_prev(si + 1, prev[(si + 1) % 2]);
     }
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj) {
@@ -798,10 +817,9 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
 #pragma unroll
       for (int v = 0; v < Mm::kAcc; ++v) {
         const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
-        const float val = ACC ? acc[si][sj][v] + prev[sj][v] : acc[si][sj][v];
         if (i < M && j < N) {
-          if constexpr ((C::STREAM & 4) != 0) __builtin_nontemporal_store(static_cast<OutT>(val), Out + i * ldo + j);
-          else Out[i * ldo + j] = static_cast<OutT>(val);
+          if constexpr ((C::STREAM & 4) != 0) __builtin_nontemporal_store(static_cast<OutT>(val[sj][v]), Out + i * ldo + j);
+          else Out[i * ldo + j] = static_cast<OutT>(val[sj][v]);
         }
       }
     }
