@@ -556,6 +556,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     return slice < nfull ? slice : nfull - 1;
   };
   std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
+  static_assert((kAhead - 1) * kLoads <= 63, "loads kept in flight must fit the 6-bit vmcnt");
   constexpr int kLoadSteps = 2;                    // MFMA steps the slice loads are spread over
   // With 16x16 tiles a fragment set is 64 VGPRs, and the scheduler's own
   // interleaving (or group hints) keeps a third set live and shuffles the
