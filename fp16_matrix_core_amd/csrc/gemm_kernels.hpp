@@ -740,6 +740,73 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
             pv[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
           }
     };
+    // Tiles wholly inside Out (and whose rows span less than 2 GiB) take a
+    // branch-free path: buffer stores (and loads) with a per-lane 32-bit
+    // offset, the row as a uniform offset and the column pair as an
+    // immediate, instead of a 64-bit address and a bounds check per element.
+    const bool interior = i0 + C::BM <= M && j0 + C::BN <= N &&
+                          int64_t(C::BM) * ldo * int64_t(sizeof(OutT)) < (int64_t(1) << 31);
+    if (interior) {
+      constexpr int kSz = sizeof(OutT);
+      constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;    // non-temporal
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(int64_t(C::BM) * ldo * kSz));
+      const int vo = ((wm * C::WTM + 8 * (lane >> 5)) * static_cast<int>(ldo) + wn * C::WTN + (lane & 31)) * kSz;
+      auto so = [&](int si, int t, int v) { return (si * 16 + 4 * t + v) * static_cast<int>(ldo) * kSz; };
+      auto ld = [&](int voff, int soff) -> float {
+        if constexpr (kSz == 4) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, voff, soff, 0));
+        } else {
+          return static_cast<float>(__builtin_bit_cast(OutT, __builtin_amdgcn_raw_buffer_load_b16(orsrc, voff, soff, 0)));
+        }
+      };
+      auto st = [&](float x, int voff, int soff) {
+        if constexpr (kSz == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), orsrc, voff, soff, kAux);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<OutT>(x)), orsrc, voff,
+                                                soff, kAux);
+        }
+      };
+      auto load_prev_fast = [&](int si, float (&pv)[kP][2][4]) {
+#pragma unroll
+        for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pv[pp][t][v] = ld(vo + 32 * pp * kSz, so(si, t, v));
+      };
+      float pf[kP][2][4];
+      if constexpr (ACC) load_prev_fast(0, pf);
+#pragma unroll
+      for (int si = 0; si < C::SI; ++si) {
+        float val[kP][2][4];
+#pragma unroll
+        for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            val[pp][0][v] = acc[si][2 * pp][v];
+            val[pp][1][v] = acc[si][2 * pp + 1][v];
+            permlane16_swap(val[pp][0][v], val[pp][1][v]);
+          }
+        if constexpr (ACC) {
+#pragma unroll
+          for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) val[pp][t][v] += pf[pp][t][v];
+          if (si + 1 < C::SI) load_prev_fast(si + 1, pf);
+        }
+#pragma unroll
+        for (int pp = 0; pp < kP; ++pp)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) st(val[pp][t][v], vo + 32 * pp * kSz, so(si, t, v));
+      }
+      return;
+    }
     float prev[kP][2][4];
     if constexpr (ACC) load_prev(0, prev);
 #pragma unroll
