@@ -856,6 +856,59 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // block si (ldo is a run-time value, so the compiler cannot prove that a
   // store does not alias a later load and would otherwise wait on each
   // load; one block ahead, only the first block's loads are waited for).
+  // Interior tiles: buffer loads/stores as in the 16x16 epilogue above.
+  {
+    const bool interior = i0 + C::BM <= M && j0 + C::BN <= N &&
+                          int64_t(C::BM) * ldo * int64_t(sizeof(OutT)) < (int64_t(1) << 31);
+    if (interior) {
+      constexpr int kSz = sizeof(OutT);
+      constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(int64_t(C::BM) * ldo * kSz));
+      // row of element v of a tile: acc_row(lane, v) = acc_row(lane, 0) + acc_row(0, v)
+      const int vo = ((wm * C::WTM + Mm::acc_row(lane, 0)) * static_cast<int>(ldo) + wn * C::WTN + Mm::acc_col(lane)) * kSz;
+      auto so = [&](int si, int v) { return (si * Mm::kM + Mm::acc_row(0, v)) * static_cast<int>(ldo) * kSz; };
+      auto ld = [&](int voff, int soff) -> float {
+        if constexpr (kSz == 4) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, voff, soff, 0));
+        } else {
+          return static_cast<float>(__builtin_bit_cast(OutT, __builtin_amdgcn_raw_buffer_load_b16(orsrc, voff, soff, 0)));
+        }
+      };
+      auto st = [&](float x, int voff, int soff) {
+        if constexpr (kSz == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), orsrc, voff, soff, kAux);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<OutT>(x)), orsrc, voff,
+                                                soff, kAux);
+        }
+      };
+      auto load_prev_fast = [&](int si, float (&pv)[C::SJ][Mm::kAcc]) {
+#pragma unroll
+        for (int sj = 0; sj < C::SJ; ++sj)
+#pragma unroll
+          for (int v = 0; v < Mm::kAcc; ++v) pv[sj][v] = ld(vo + sj * Mm::kM * kSz, so(si, v));
+      };
+      float pf[2][C::SJ][Mm::kAcc];
+      if constexpr (ACC) load_prev_fast(0, pf[0]);
+#pragma unroll
+      for (int si = 0; si < C::SI; ++si) {
+        float val[C::SJ][Mm::kAcc];
+#pragma unroll
+        for (int sj = 0; sj < C::SJ; ++sj)
+#pragma unroll
+          for (int v = 0; v < Mm::kAcc; ++v) val[sj][v] = ACC ? acc[si][sj][v] + pf[si % 2][sj][v] : acc[si][sj][v];
+        if constexpr (ACC) {
+          if (si + 1 < C::SI) load_prev_fast(si + 1, pf[(si + 1) % 2]);
+        }
+#pragma unroll
+        for (int sj = 0; sj < C::SJ; ++sj)
+#pragma unroll
+          for (int v = 0; v < Mm::kAcc; ++v) st(val[sj][v], vo + sj * Mm::kM * kSz, so(si, v));
+      }
+      return;
+    }
+  }
   auto load_prev = [&](int si, float (&pv)[C::SJ][Mm::kAcc]) {
 #pragma unroll
     for (int sj = 0; sj < C::SJ; ++sj) {
