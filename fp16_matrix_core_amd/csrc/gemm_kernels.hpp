@@ -723,8 +723,8 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // row pieces (128 bytes of fp32) instead of four 16-column ones.
   if constexpr (C::MI == 16 && C::SJ % 2 == 0) {
     constexpr int kP = C::SJ / 2;
-    const int64_t jb = j0 + wn * C::WTN + (lane & 31);
-    auto row_base = [&](int si) { return i0 + wm * C::WTM + si * 16 + 8 * (lane >> 5); };
+    const int64_t jb = j0 + wn * C::WTN + mfma16::swapped_col(lane);
+    auto row_base = [&](int si) { return i0 + wm * C::WTM + si * 16 + mfma16::swapped_row(lane, 0, 0); };
     // When accumulating, row block si+1's previous values are loaded before
     // block si is stored, so that only the first block waits for its loads.
     // (The rows differ, so the order of these loads and stores is free.)
@@ -736,7 +736,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
+            const int64_t i = ib + mfma16::swapped_row(0, t, v), j = jb + 32 * pp;
             pv[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
           }
     };
@@ -751,8 +751,10 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;    // non-temporal
       const __amdgpu_buffer_rsrc_t orsrc =
           make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(int64_t(C::BM) * ldo * kSz));
-      const int vo = ((wm * C::WTM + 8 * (lane >> 5)) * static_cast<int>(ldo) + wn * C::WTN + (lane & 31)) * kSz;
-      auto so = [&](int si, int t, int v) { return (si * 16 + 4 * t + v) * static_cast<int>(ldo) * kSz; };
+      // swapped_row(l, t, v) = swapped_row(l, 0, 0) + swapped_row(0, t, v)
+      const int vo = ((wm * C::WTM + mfma16::swapped_row(lane, 0, 0)) * static_cast<int>(ldo) + wn * C::WTN +
+                      mfma16::swapped_col(lane)) * kSz;
+      auto so = [&](int si, int t, int v) { return (si * 16 + mfma16::swapped_row(0, t, v)) * static_cast<int>(ldo) * kSz; };
       auto ld = [&](int voff, int soff) -> float {
         if constexpr (kSz == 4) {
           return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, voff, soff, 0));
@@ -836,7 +838,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t i = ib + 4 * t + v, j = jb + 32 * pp;
+            const int64_t i = ib + mfma16::swapped_row(0, t, v), j = jb + 32 * pp;
             if (i < M && j < N) {
               if constexpr ((C::STREAM & 4) != 0)
                 __builtin_nontemporal_store(static_cast<OutT>(val[pp][t][v]), Out + i * ldo + j);

@@ -157,6 +157,13 @@ FP16MC_HD constexpr int operand_row(int lane) { return lane & 15; }
 FP16MC_HD constexpr int operand_k(int lane, int e) { return 8 * (lane >> 4) + e; }
 FP16MC_HD constexpr int acc_row(int lane, int v) { return 4 * (lane >> 4) + v; }
 FP16MC_HD constexpr int acc_col(int lane, int /*v*/) { return lane & 15; }
+// v_permlane16_swap_b32 x, y trades 16-lane rows 1 and 3 of x with rows 0
+// and 2 of y.  Applied to element v of two horizontally adjacent tiles (the
+// left one's register as x), register t (0: x, 1: y), element v of lane l
+// then holds row swapped_row(l, t, v), column swapped_col(l) of the 16x32
+// pair: 32 consecutive columns of one row per half-wavefront.
+FP16MC_HD constexpr int swapped_row(int lane, int t, int v) { return 4 * t + v + 8 * (lane >> 5); }
+FP16MC_HD constexpr int swapped_col(int lane) { return lane & 31; }
 }  // namespace mfma16
 
 // ---------------------------------------------------------------------------

@@ -297,6 +297,34 @@ int main() {
       for (int e = 0; e < 8; ++e) ops16.insert({mfma16::operand_row(l), mfma16::operand_k(l, e)});
     CHECK(ops16.size() == 16 * 32, "mfma16 operand map not a bijection");
   }
+  // v_permlane16_swap (16-lane rows 1 and 3 of x trade with rows 0 and 2 of y, as probed on
+  // gfx950) on the accumulators of two adjacent 16x16 tiles gives the swapped_row/col map
+  for (int v = 0; v < mfma16::kAcc; ++v) {
+    int x[64][2], y[64][2];   // (row, col) in the 16x32 pair held by lane l
+    for (int l = 0; l < 64; ++l) {
+      x[l][0] = mfma16::acc_row(l, v), x[l][1] = mfma16::acc_col(l, v);
+      y[l][0] = mfma16::acc_row(l, v), y[l][1] = 16 + mfma16::acc_col(l, v);
+    }
+    int xs[64][2], ys[64][2];
+    for (int l = 0; l < 64; ++l) {
+      const int row = l >> 4, i = l & 15;
+      for (int k = 0; k < 2; ++k) {
+        xs[l][k] = (row & 1) == 0 ? x[l][k] : y[16 * (row - 1) + i][k];
+        ys[l][k] = (row & 1) == 0 ? x[16 * (row + 1) + i][k] : y[l][k];
+      }
+    }
+    for (int l = 0; l < 64; ++l) {
+      CHECK(xs[l][0] == mfma16::swapped_row(l, 0, v) && xs[l][1] == mfma16::swapped_col(l), "swap x lane %d v %d", l, v);
+      CHECK(ys[l][0] == mfma16::swapped_row(l, 1, v) && ys[l][1] == mfma16::swapped_col(l), "swap y lane %d v %d", l, v);
+    }
+  }
+  {
+    std::set<std::pair<int, int>> cells;
+    for (int l = 0; l < 64; ++l)
+      for (int t = 0; t < 2; ++t)
+        for (int v = 0; v < 4; ++v) cells.insert({mfma16::swapped_row(l, t, v), mfma16::swapped_col(l)});
+    CHECK(cells.size() == 16 * 32, "swapped map not a bijection of the 16x32 pair");
+  }
   // m8n8: each 32-lane half covers the 8 rows x 4 column pairs once; images are bijections
   for (int num : {1, 2, 4})
     for (int col = 0; col < 2; ++col) {
