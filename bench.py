@@ -17,7 +17,9 @@ Besides the headline, the same line carries:
                 same workload, timed on this host;
   secondary     frag_copy (2^20 tiles, every num / layout / direction) in GB/s
                 against HBM bandwidth with rotating buffers, the batched
-                4096 x (128x64x64) product and the 16384x8x16384 skinny product.
+                4096 x (128x64x64) product, the 16384x8x16384 skinny product,
+                the single 16x8x16 tile and 128x64x64 workgroup (us per call),
+                and the 8192^3 launch with other types and storage orders.
 """
 
 import argparse
@@ -184,6 +186,28 @@ def bench_skinny(torch, f, stream, reps=20):
             "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
+def bench_small(torch, f, stream, reps=200):
+    """The single 16x8x16 tile and the single 128x64x64 workgroup: time per call
+    (launch-latency bound) through the raw entry point, inputs resident."""
+    from fp16_matrix_core_amd import inputs
+    out = {}
+    A1, B1 = inputs.single_tile()
+    A2, B2 = inputs.single_workgroup()[:2]
+    sp = stream.cuda_stream
+    for name, (A, B) in (("single_tile_16x8x16", (A1, B1)), ("single_workgroup_128x64x64", (A2, B2))):
+        (M, K), N = A.shape, B.shape[0]
+        a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        o = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+        def call():
+            f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), o.data_ptr(), M, N, K, K, K, N, sp)
+        for _ in range(10):
+            call()
+        ms = StreamTimer(torch, stream).time(call, reps)
+        out[name] = {"plan": f.plan(M, N, K), "us": round(ms * 1e3, 2)}
+    return out
+
+
 def bench_types(torch, f, stream, a, b, reps=20):
     """The 8192^3 launch with bfloat16 operands, 16-bit outputs and accumulation (gemm_nt_ex)."""
     from fp16_matrix_core_amd import inputs
@@ -331,6 +355,7 @@ def main():
         result["secondary"] = {"frag_copy": bench_frag(torch, f, stream),
                                "batched_4096x128x64x64": bench_batched(torch, f, stream),
                                "skinny_16384x8x16384": bench_skinny(torch, f, stream),
+                               "small": bench_small(torch, f, stream),
                                "gemm_8192_types": bench_types(torch, f, stream, a, b),
                                "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
     if not args.no_cpu_baseline:
