@@ -47,10 +47,16 @@ def log(*a):
 
 
 def gemm_source_hash():
+    """Hash of the GEMM kernel sources with comments and whitespace removed, so that
+    the counter summary stays matched to the kernel across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for p in GEMM_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -19,9 +19,10 @@
 //                   row fetch one whole 128-byte line, which halves the L2
 //                   requests of BK = 32 (two half-line requests per line).
 //   LDS -> VGPR     one ds_read_b128 per lane per operand fragment: the 8
-//                   consecutive-K fp16 that v_mfma_f32_32x32x16_f16 (or
-//                   v_mfma_f32_16x16x32_f16) takes from each lane.  Both
-//                   operands are K-contiguous (NT), so no transpose is needed.
+//                   consecutive-K fp16 that v_mfma_f32_16x16x32_f16 (or
+//                   v_mfma_f32_32x32x16_f16) takes from each lane, for a
+//                   K-contiguous operand; an operand stored MN-contiguous is
+//                   staged as it lies and read with two ds_read_b64_tr_b16.
 //   MFMA            A's fragment is the instruction's first operand, B's
 //                   the second, so in each accumulator register consecutive
 //                   lanes hold consecutive columns of one output row (32 for
@@ -34,7 +35,8 @@
 //                   tiles an XCD runs together share A and B panels in L2.
 //   edges           rows past M or N are clamped on load (their results are
 //                   never stored); K past the end is zero-filled; the
-//                   epilogue masks columns past N and rows past M.
+//                   epilogue masks columns past N and rows past M (tiles
+//                   wholly inside Out store without masks).
 
 #pragma once
 
@@ -162,9 +164,10 @@ using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 0, 16>;
 using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
 // 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
-// Every CU finishes its tile at the same moment, so each wave of tiles ends
-// in one HBM-bound burst of output writes (about 6% of the 8192^3 time);
-// non-temporal stores shorten it by about a third.
+// Each tile ends with its 256 KiB of output written by one CU, which its
+// write path takes about 15 us to drain (about 8% of a tile at 8192^3, in
+// every wave of tiles); non-temporal stores and, for interior tiles,
+// stores without per-element bounds checks shorten it.
 // 16x16x32 instructions: with random operands the chip is power-bound, and
 // the 16x16 form sustains about 17% more MFMA throughput than the 32x32 one
 // (it moves half the accumulator per flop); 8192^3 is 5-8% faster with it.
