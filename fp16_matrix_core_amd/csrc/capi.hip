@@ -98,9 +98,11 @@ int gemm_ex(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64
   const int64_t grid = fp16mc::gemm_plan_grid(plan, M, N, batch);
   if (grid > kMaxGrid) return fail(FP16MC_EINVAL, "problem needs %lld workgroups (limit %lld)",
                                    (long long)grid, (long long)kMaxGrid);
-  if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb, a_mn, b_mn))
-    return fail(FP16MC_EINVAL, "a %s tile of lda=%lld / ldb=%lld rows spans 2^32 bytes or more",
-                fp16mc::gemm_plan_name(plan, a_mn, b_mn), (long long)lda, (long long)ldb);
+  if (!fp16mc::gemm_plan_fits_offsets(plan, K, lda, ldb, ldo, out_type == FP16MC_F32 ? 4 : 2, a_mn, b_mn))
+    return fail(FP16MC_EINVAL,
+                "a %s tile spans too many bytes (operand rows of lda=%lld / ldb=%lld must stay below 2^32, "
+                "output rows of ldo=%lld below 2^31)",
+                fp16mc::gemm_plan_name(plan, a_mn, b_mn), (long long)lda, (long long)ldb, (long long)ldo);
   fp16mc::GemmProblem p{A,      B,       Out,     M,       N,       K,
                         lda,    ldb,     ldo,     batch,   strideA, strideB,
                         strideO, static_cast<fp16mc::Dtype>(ab_type), static_cast<fp16mc::Dtype>(out_type),

@@ -34,9 +34,10 @@
 //   scheduler       XCD-contiguous ranges of tile ids, grouped so that the
 //                   tiles an XCD runs together share A and B panels in L2.
 //   edges           rows past M or N are clamped on load (their results are
-//                   never stored); K past the end is zero-filled; the
-//                   epilogue masks columns past N and rows past M (tiles
-//                   wholly inside Out store without masks).
+//                   never stored); K past the end is zero-filled; Out is
+//                   accessed through a buffer that ends at the tile's last
+//                   valid element, with columns past N given an offset
+//                   outside it, so every tile stores through one path.
 
 #pragma once
 
@@ -109,14 +110,6 @@ struct Mma<16> {
   static __device__ __forceinline__ int tr_m(int lane) { return 4 * (lane & 3); }
 };
 
-// One output element: the fp32 sum, plus the element's previous value when
-// accumulating, stored as fp32 or rounded to nearest-even fp16 / bf16.
-template <class OutT, bool ACC>
-__device__ __forceinline__ void store_out(OutT* p, float v) {
-  if constexpr (ACC) v += static_cast<float>(*p);
-  *p = static_cast<OutT>(v);
-}
-
 // BM x BN output tile per workgroup, WM x WN wavefronts, each owning a
 // (BM/WM) x (BN/WN) sub-tile made of MI x MI MFMA tiles (MI = 32: 32x32x16,
 // MI = 16: 16x16x32).  K advances in slices of BK (32 or 64) held in a ring
@@ -166,8 +159,8 @@ using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 160 KiB); measured 6-7% faster at 8192^3 than 32-wide slices in four stages.
 // Each tile ends with its 256 KiB of output written by one CU, which its
 // write path takes about 15 us to drain (about 8% of a tile at 8192^3, in
-// every wave of tiles); non-temporal stores and, for interior tiles,
-// stores without per-element bounds checks shorten it.
+// every wave of tiles); non-temporal stores and buffer stores without
+// per-element bounds checks shorten it.
 // 16x16x32 instructions: with random operands the chip is power-bound, and
 // the 16x16 form sustains about 17% more MFMA throughput than the 32x32 one
 // (it moves half the accumulator per flop); 8192^3 is 5-8% faster with it.
@@ -314,11 +307,13 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // ---- tile scheduler -------------------------------------------------------
   const uint32_t lin = sched::xcd_remap(blockIdx.x, static_cast<uint32_t>(total));
   const uint32_t per_problem = static_cast<uint32_t>(tiles_m * tiles_n);
-  const uint32_t b = lin / per_problem;
+  const uint32_t b = __builtin_amdgcn_readfirstlane(lin / per_problem);
   const sched::Tile tile = sched::grouped_tile(lin - b * per_problem, static_cast<uint32_t>(tiles_m),
                                                static_cast<uint32_t>(tiles_n), C::GROUP_M);
-  const int64_t i0 = static_cast<int64_t>(tile.m) * C::BM;
-  const int64_t j0 = static_cast<int64_t>(tile.n) * C::BN;
+  // Integer division runs on the vector unit: name the (uniform) results as
+  // scalars so that the tile origin does not hold vector registers.
+  const int64_t i0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tile.m)) * C::BM;
+  const int64_t j0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tile.n)) * C::BN;
   A += b * sA;
   B += b * sB;
   Out += b * sO;
@@ -537,6 +532,64 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     asm volatile("s_barrier" ::: "memory");
   };
 
+  // ---- Out tile addressing (accumulate prologue and epilogue) -------------------
+  // Every access to Out is a buffer access relative to the tile's origin,
+  // with the whole offset (lane, column block and row) in the per-lane
+  // offset register, which the buffer's range check covers.  The buffer ends
+  // at the last valid element of the tile's last valid row, so rows past M
+  // read as zero and their stores are dropped; lanes whose column is past N
+  // take an offset beyond any buffer for that column block.  (The host keeps
+  // BM * ldo * sizeof(OutT) below 2^31, so no offset wraps, and every tile
+  // takes this one path.)
+  constexpr int kSz = sizeof(OutT);
+  constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;    // non-temporal stores
+  constexpr unsigned kOff = 0x80000000u;               // beyond every tile's buffer
+  const int64_t o_rows = (M - i0) < C::BM ? (M - i0) : C::BM;
+  const int o_cols = static_cast<int>((N - j0) < C::BN ? (N - j0) : C::BN);
+  const __amdgpu_buffer_rsrc_t orsrc =
+      make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(((o_rows - 1) * ldo + o_cols) * kSz));
+  const int ldo_b = static_cast<int>(ldo) * kSz;       // bytes per row of Out
+  // Per-lane offsets of column blocks 0 .. NC-1 of width CW, for a lane at
+  // tile row `row` and column `col` of block 0.
+  auto col_offsets = [&](unsigned* off, int nc, int cw, int row, int col) FP16MC_INLINE {
+#pragma unroll
+    for (int c = 0; c < nc; ++c)
+      off[c] = col + c * cw < o_cols ? static_cast<unsigned>(row * ldo_b + (col + c * cw) * kSz) : kOff;
+  };
+  // Register layout of the stores.  16x16 tiles with an even SJ: the
+  // registers of each pair of horizontally adjacent tiles (sj = 2p, 2p+1)
+  // are regrouped with v_permlane16_swap (16-lane rows 1 and 3 of the first
+  // operand trade places with rows 0 and 2 of the second), so that in
+  // register t, element v, lane l holds Out[i][j] with
+  // i = i0 + wm*WTM + 16 si + 4t + v + 8(l/32), j = j0 + wn*WTN + 32p + l%32:
+  // each store covers two whole 32-column row pieces (128 bytes of fp32)
+  // instead of four 16-column ones.  Otherwise element v of lane l in tile
+  // (si, sj) is Out[i][j] with i = i0 + wm*WTM + MI si + acc_row(l, v),
+  // j = j0 + wn*WTN + MI sj + acc_col(l) (two whole 128-byte row segments per
+  // store with 32x32 tiles).  Below, (c, t, v) names element v of register t
+  // of column block c (a tile pair p, or a tile sj with t = 0).
+  constexpr bool kSwap = C::MI == 16 && C::SJ % 2 == 0;
+  constexpr int kNC = kSwap ? C::SJ / 2 : C::SJ;   // column blocks
+  constexpr int kNT = kSwap ? 2 : 1;               // registers per column block
+  constexpr int kNV = kSwap ? 4 : Mm::kAcc;        // elements per register
+  constexpr int kCW = kSwap ? 32 : Mm::kM;         // columns per block
+  typedef float OutBlock[kNC][kNT][kNV];           // one row block's values
+  auto elem_row = [&](int t, int v) { return kSwap ? mfma16::swapped_row(0, t, v) : Mm::acc_row(0, v); };
+  auto so = [&](int si, int t, int v) { return (si * Mm::kM + elem_row(t, v)) * ldo_b; };
+  auto acc_to_block = [&](int si, OutBlock& val) FP16MC_INLINE {
+#pragma unroll
+    for (int c = 0; c < kNC; ++c)
+#pragma unroll
+      for (int v = 0; v < kNV; ++v) {
+        if constexpr (kSwap) {
+          val[c][0][v] = acc[si][2 * c][v];
+          val[c][1][v] = acc[si][2 * c + 1][v];
+          permlane16_swap(val[c][0][v], val[c][1][v]);
+        } else {
+          val[c][0][v] = acc[si][c][v];
+        }
+      }
+  };
   // ---- K loop --------------------------------------------------------------------
   // Full slice s lives in stage s % S of an S-stage ring.  Slices s+1 ..
   // s+S-2 are already in flight when phase s begins; phase s issues slice
@@ -717,238 +770,69 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     }
   }
 
-  // ---- epilogue, 16x16 tiles: the registers of each pair of horizontally
-  // adjacent tiles (sj = 2p, 2p+1) are regrouped with v_permlane16_swap
-  // (16-lane rows 1 and 3 of the first operand trade places with rows 0
-  // and 2 of the second), so that in register t, element v, lane l holds
-  // Out[i][j] with i = i0 + wm*WTM + 16 si + 4t + v + 8(l/32) and
-  // j = j0 + wn*WTN + 32p + l%32: each store writes two whole 32-column
-  // row pieces (128 bytes of fp32) instead of four 16-column ones.
-  if constexpr (C::MI == 16 && C::SJ % 2 == 0) {
-    constexpr int kP = C::SJ / 2;
-    const int64_t jb = j0 + wn * C::WTN + mfma16::swapped_col(lane);
-    auto row_base = [&](int si) { return i0 + wm * C::WTM + si * 16 + mfma16::swapped_row(lane, 0, 0); };
-    // When accumulating, row block si+1's previous values are loaded before
-    // block si is stored, so that only the first block waits for its loads.
-    // (The rows differ, so the order of these loads and stores is free.)
-    auto load_prev = [&](int si, float (&pv)[kP][2][4]) {
-      const int64_t ib = row_base(si);
+  // ---- epilogue: each row block's values in the (c, t, v) layout, plus the
+  // block's previous values when accumulating, stored as fp32 or rounded to
+  // nearest-even fp16 / bf16.  The previous values are loaded kPre row
+  // blocks ahead of their use: loads and stores share one in-order
+  // completion counter, so waiting for a block's loads also waits for every
+  // store issued before them, and a deeper prefetch lets the stores of the
+  // last blocks stay in flight meanwhile (the registers of the blocks already
+  // stored hold the prefetched values).  Measured at 8192^3 (16x16 tiles,
+  // 32 values per block): three blocks ahead 4% faster than one for fp32,
+  // two as good as three for 16 bits.  The depth is set in values, so that
+  // the 64-value blocks of 32x32 tiles stay one block ahead (deeper, their
+  // 256x256 kernels spill).
+  unsigned vs[kNC];
+  col_offsets(vs, kNC, kCW, wm * C::WTM + (kSwap ? mfma16::swapped_row(lane, 0, 0) : Mm::acc_row(lane, 0)),
+              wn * C::WTN + (kSwap ? mfma16::swapped_col(lane) : Mm::acc_col(lane)));
+  constexpr int kBlockVals = kNC * kNT * kNV;        // loads per row block
+  constexpr int kPreVals = kSz == 4 ? 96 : 64;       // values in flight
+  constexpr int kPre = kPreVals / kBlockVals < 1 ? 1 : (kPreVals / kBlockVals > C::SI ? C::SI : kPreVals / kBlockVals);
+  OutBlock prev[kPre];
+  auto load_block = [&](int si, OutBlock& pv) FP16MC_INLINE {
 #pragma unroll
-      for (int pp = 0; pp < kP; ++pp)
+    for (int c = 0; c < kNC; ++c)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < kNT; ++t)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t i = ib + mfma16::swapped_row(0, t, v), j = jb + 32 * pp;
-            pv[pp][t][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
-          }
-    };
-    // Tiles wholly inside Out (and whose rows span less than 2 GiB) take a
-    // branch-free path: buffer stores (and loads) with a per-lane 32-bit
-    // offset, the row as a uniform offset and the column pair as an
-    // immediate, instead of a 64-bit address and a bounds check per element.
-    const bool interior = i0 + C::BM <= M && j0 + C::BN <= N &&
-                          int64_t(C::BM) * ldo * int64_t(sizeof(OutT)) < (int64_t(1) << 31);
-    if (interior) {
-      constexpr int kSz = sizeof(OutT);
-      constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;    // non-temporal
-      const __amdgpu_buffer_rsrc_t orsrc =
-          make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(int64_t(C::BM) * ldo * kSz));
-      // swapped_row(l, t, v) = swapped_row(l, 0, 0) + swapped_row(0, t, v)
-      const int vo = ((wm * C::WTM + mfma16::swapped_row(lane, 0, 0)) * static_cast<int>(ldo) + wn * C::WTN +
-                      mfma16::swapped_col(lane)) * kSz;
-      auto so = [&](int si, int t, int v) { return (si * 16 + mfma16::swapped_row(0, t, v)) * static_cast<int>(ldo) * kSz; };
-      auto ld = [&](int voff, int soff) -> float {
-        if constexpr (kSz == 4) {
-          return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, voff, soff, 0));
-        } else {
-          return static_cast<float>(__builtin_bit_cast(OutT, __builtin_amdgcn_raw_buffer_load_b16(orsrc, voff, soff, 0)));
+        for (int v = 0; v < kNV; ++v) {
+          if constexpr (kSz == 4)
+            pv[c][t][v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, vs[c] + so(si, t, v), 0, 0));
+          else
+            pv[c][t][v] = static_cast<float>(
+                __builtin_bit_cast(OutT, __builtin_amdgcn_raw_buffer_load_b16(orsrc, vs[c] + so(si, t, v), 0, 0)));
         }
-      };
-      auto st = [&](float x, int voff, int soff) {
-        if constexpr (kSz == 4) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), orsrc, voff, soff, kAux);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<OutT>(x)), orsrc, voff,
-                                                soff, kAux);
-        }
-      };
-      auto load_prev_fast = [&](int si, float (&pv)[kP][2][4]) {
-#pragma unroll
-        for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) pv[pp][t][v] = ld(vo + 32 * pp * kSz, so(si, t, v));
-      };
-      float pf[kP][2][4];
-      if constexpr (ACC) load_prev_fast(0, pf);
-#pragma unroll
-      for (int si = 0; si < C::SI; ++si) {
-        float val[kP][2][4];
-#pragma unroll
-        for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            val[pp][0][v] = acc[si][2 * pp][v];
-            val[pp][1][v] = acc[si][2 * pp + 1][v];
-            permlane16_swap(val[pp][0][v], val[pp][1][v]);
-          }
-        if constexpr (ACC) {
-#pragma unroll
-          for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) val[pp][t][v] += pf[pp][t][v];
-          if (si + 1 < C::SI) load_prev_fast(si + 1, pf);
-        }
-#pragma unroll
-        for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) st(val[pp][t][v], vo + 32 * pp * kSz, so(si, t, v));
-      }
-      return;
-    }
-    float prev[kP][2][4];
-    if constexpr (ACC) load_prev(0, prev);
-#pragma unroll
-    for (int si = 0; si < C::SI; ++si) {
-      float val[kP][2][4];
-#pragma unroll
-      for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          val[pp][0][v] = acc[si][2 * pp][v];
-          val[pp][1][v] = acc[si][2 * pp + 1][v];
-          permlane16_swap(val[pp][0][v], val[pp][1][v]);
-        }
-      const int64_t ib = row_base(si);
-      if constexpr (ACC) {
-#pragma unroll
-        for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) val[pp][t][v] += prev[pp][t][v];
-        if (si + 1 < C::SI) load_prev(si + 1, prev);
-      }
-#pragma unroll
-      for (int pp = 0; pp < kP; ++pp)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t i = ib + mfma16::swapped_row(0, t, v), j = jb + 32 * pp;
-            if (i < M && j < N) {
-              if constexpr ((C::STREAM & 4) != 0)
-                __builtin_nontemporal_store(static_cast<OutT>(val[pp][t][v]), Out + i * ldo + j);
-              else
-                Out[i * ldo + j] = static_cast<OutT>(val[pp][t][v]);
-            }
-          }
-    }
-    return;
-  }
-
-  // ---- epilogue: element v of lane l in tile (si, sj) is Out[i][j] with
-  // i = i0 + wm*WTM + MI si + acc_row(l, v), j = j0 + wn*WTN + MI sj + acc_col(l):
-  // with 32x32 tiles one dword store per v writes two whole 128-byte row
-  // segments, with 16x16 tiles four 64-byte ones.  When accumulating, the
-  // previous values of row block si+1 are all loaded before any store of
-  // block si (ldo is a run-time value, so the compiler cannot prove that a
-  // store does not alias a later load and would otherwise wait on each
-  // load; one block ahead, only the first block's loads are waited for).
-  // Interior tiles: buffer loads/stores as in the 16x16 epilogue above.
-  {
-    const bool interior = i0 + C::BM <= M && j0 + C::BN <= N &&
-                          int64_t(C::BM) * ldo * int64_t(sizeof(OutT)) < (int64_t(1) << 31);
-    if (interior) {
-      constexpr int kSz = sizeof(OutT);
-      constexpr int kAux = (C::STREAM & 4) != 0 ? 2 : 0;
-      const __amdgpu_buffer_rsrc_t orsrc =
-          make_rsrc(Out + i0 * ldo + j0, static_cast<unsigned>(int64_t(C::BM) * ldo * kSz));
-      // row of element v of a tile: acc_row(lane, v) = acc_row(lane, 0) + acc_row(0, v)
-      const int vo = ((wm * C::WTM + Mm::acc_row(lane, 0)) * static_cast<int>(ldo) + wn * C::WTN + Mm::acc_col(lane)) * kSz;
-      auto so = [&](int si, int v) { return (si * Mm::kM + Mm::acc_row(0, v)) * static_cast<int>(ldo) * kSz; };
-      auto ld = [&](int voff, int soff) -> float {
-        if constexpr (kSz == 4) {
-          return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(orsrc, voff, soff, 0));
-        } else {
-          return static_cast<float>(__builtin_bit_cast(OutT, __builtin_amdgcn_raw_buffer_load_b16(orsrc, voff, soff, 0)));
-        }
-      };
-      auto st = [&](float x, int voff, int soff) {
-        if constexpr (kSz == 4) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), orsrc, voff, soff, kAux);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<OutT>(x)), orsrc, voff,
-                                                soff, kAux);
-        }
-      };
-      auto load_prev_fast = [&](int si, float (&pv)[C::SJ][Mm::kAcc]) {
-#pragma unroll
-        for (int sj = 0; sj < C::SJ; ++sj)
-#pragma unroll
-          for (int v = 0; v < Mm::kAcc; ++v) pv[sj][v] = ld(vo + sj * Mm::kM * kSz, so(si, v));
-      };
-      float pf[2][C::SJ][Mm::kAcc];
-      if constexpr (ACC) load_prev_fast(0, pf[0]);
-#pragma unroll
-      for (int si = 0; si < C::SI; ++si) {
-        float val[C::SJ][Mm::kAcc];
-#pragma unroll
-        for (int sj = 0; sj < C::SJ; ++sj)
-#pragma unroll
-          for (int v = 0; v < Mm::kAcc; ++v) val[sj][v] = ACC ? acc[si][sj][v] + pf[si % 2][sj][v] : acc[si][sj][v];
-        if constexpr (ACC) {
-          if (si + 1 < C::SI) load_prev_fast(si + 1, pf[(si + 1) % 2]);
-        }
-#pragma unroll
-        for (int sj = 0; sj < C::SJ; ++sj)
-#pragma unroll
-          for (int v = 0; v < Mm::kAcc; ++v) st(val[sj][v], vo + sj * Mm::kM * kSz, so(si, v));
-      }
-      return;
-    }
-  }
-  auto load_prev = [&](int si, float (&pv)[C::SJ][Mm::kAcc]) {
-#pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj) {
-      const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
-#pragma unroll
-      for (int v = 0; v < Mm::kAcc; ++v) {
-        const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
-        pv[sj][v] = (i < M && j < N) ? static_cast<float>(Out[i * ldo + j]) : 0.0f;
-      }
-    }
   };
-  float prev[2][C::SJ][Mm::kAcc];
-  if constexpr (ACC) load_prev(0, prev[0]);
+  if constexpr (ACC) {
+#pragma unroll
+    for (int si = 0; si < kPre; ++si) load_block(si, prev[si]);
+  }
 #pragma unroll
   for (int si = 0; si < C::SI; ++si) {
-    float val[C::SJ][Mm::kAcc];
-#pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj)
-#pragma unroll
-      for (int v = 0; v < Mm::kAcc; ++v) val[sj][v] = ACC ? acc[si][sj][v] + prev[si % 2][sj][v] : acc[si][sj][v];
+    OutBlock val;
+    acc_to_block(si, val);
     if constexpr (ACC) {
-      if (si + 1 < C::SI) load_prev(si + 1, prev[(si + 1) % 2]);
+#pragma unroll
+      for (int c = 0; c < kNC; ++c)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+#pragma unroll
+          for (int v = 0; v < kNV; ++v) val[c][t][v] += prev[si % kPre][c][t][v];
+      if (si + kPre < C::SI) load_block(si + kPre, prev[si % kPre]);
     }
 #pragma unroll
-    for (int sj = 0; sj < C::SJ; ++sj) {
-      const int64_t j = j0 + wn * C::WTN + sj * Mm::kM + Mm::acc_col(lane);
+    for (int c = 0; c < kNC; ++c)
 #pragma unroll
-      for (int v = 0; v < Mm::kAcc; ++v) {
-        const int64_t i = i0 + wm * C::WTM + si * Mm::kM + Mm::acc_row(lane, v);
-        if (i < M && j < N) {
-          if constexpr ((C::STREAM & 4) != 0) __builtin_nontemporal_store(static_cast<OutT>(val[sj][v]), Out + i * ldo + j);
-          else Out[i * ldo + j] = static_cast<OutT>(val[sj][v]);
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+          if constexpr (kSz == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val[c][t][v]), orsrc,
+                                                  vs[c] + so(si, t, v), 0, kAux);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<OutT>(val[c][t][v])),
+                                                  orsrc, vs[c] + so(si, t, v), 0, kAux);
         }
-      }
-    }
   }
 }
 

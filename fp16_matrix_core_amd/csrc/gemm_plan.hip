@@ -102,23 +102,26 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
 // offsets: a K-contiguous tile spans W - 1 rows plus K values; an
 // MN-contiguous one is re-based for every slice and spans BK rows.
 template <class C>
-bool fits_offsets(int64_t K, int64_t lda, int64_t ldb, bool a_mn, bool b_mn) {
+bool fits_offsets(int64_t K, int64_t lda, int64_t ldb, int64_t ldo, int64_t out_bytes, bool a_mn, bool b_mn) {
   const int64_t limit = int64_t(1) << 32;
   const int64_t a = a_mn ? 2 * C::BK * lda : 2 * ((C::BM - 1) * lda + K);
   const int64_t b = b_mn ? 2 * C::BK * ldb : 2 * ((C::BN - 1) * ldb + K);
-  return a < limit && b < limit;
+  // Out is addressed from each tile's origin with signed 32-bit row offsets
+  const int64_t o = int64_t(C::BM) * ldo * out_bytes;
+  return a < limit && b < limit && o < (int64_t(1) << 31);
 }
 
-bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, bool a_mn, bool b_mn) {
+bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, int64_t ldo, int64_t out_bytes,
+                            bool a_mn, bool b_mn) {
   switch (plan) {
-    case GemmPlan::kWave32: return fits_offsets<CfgWave32>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWg128x64: return fits_offsets<CfgWg128x64>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWg256: return fits_offsets<CfgWg256>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kTall: return fits_offsets<CfgTall>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWg128x64Stream: return fits_offsets<CfgWg128x64Stream>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWg256x128: return fits_offsets<CfgWg256x128>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWg128x128: return fits_offsets<CfgWg128x128>(K, lda, ldb, a_mn, b_mn);
-    case GemmPlan::kWide: return fits_offsets<CfgWide>(K, lda, ldb, a_mn, b_mn);
+    case GemmPlan::kWave32: return fits_offsets<CfgWave32>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg128x64: return fits_offsets<CfgWg128x64>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg256: return fits_offsets<CfgWg256>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kTall: return fits_offsets<CfgTall>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg128x64Stream: return fits_offsets<CfgWg128x64Stream>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg256x128: return fits_offsets<CfgWg256x128>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg128x128: return fits_offsets<CfgWg128x128>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWide: return fits_offsets<CfgWide>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
     default: return true;
   }
 }

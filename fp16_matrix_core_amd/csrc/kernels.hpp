@@ -54,9 +54,11 @@ hipError_t launch_gemm_nt(GemmPlan plan, const GemmProblem& p, hipStream_t strea
 hipError_t launch_gemm_nn(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_tt(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_tn(GemmPlan plan, const GemmProblem& p, hipStream_t stream);
-// True when every operand tile of the plan spans fewer than 2^32 bytes (the
-// kernels address a tile through a buffer descriptor with 32-bit offsets).
-bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, bool a_mn, bool b_mn);
+// True when every operand tile of the plan spans fewer than 2^32 bytes and a
+// tile's rows of Out (out_bytes per element) fewer than 2^31 (the kernels
+// address a tile through a buffer descriptor with 32-bit offsets).
+bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, int64_t ldo, int64_t out_bytes,
+                            bool a_mn, bool b_mn);
 
 // Fragment copy; `groups` = num_tiles / num.
 hipError_t launch_frag_copy(const void* src, void* dst, int64_t groups, int num, bool col_major,

@@ -55,7 +55,9 @@ typedef enum {
  *   aligned and ldo a multiple of 4.
  * Size limit (else FP16MC_EINVAL): the kernels address each operand tile
  *   (up to 256 rows) with 32-bit byte offsets, so 2*(255*lda + K) and
- *   2*(255*ldb + K) must stay below 2^32 (about lda, ldb < 8.4e6).
+ *   2*(255*ldb + K) must stay below 2^32 (about lda, ldb < 8.4e6), and each
+ *   output tile with signed 32-bit offsets: 256*ldo*4 < 2^31 (ldo < 2.1e6;
+ *   256*ldo*2 for 16-bit outputs).
  * M == 0 or N == 0: nothing is enqueued, FP16MC_OK.  K == 0: Out = 0.
  * Operands may not overlap Out.
  */

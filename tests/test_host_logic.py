@@ -80,6 +80,17 @@ def test_gemm_rejects_tiles_beyond_32bit_offsets(L):
     assert "2^32" in L.fp16mc_last_error().decode()
 
 
+def test_gemm_rejects_output_tiles_beyond_31bit_offsets(L):
+    # 8192^3 runs 256x256 tiles: 256 rows of Out at ldo = 2^21 fp32 or 2^22
+    # fp16 elements span 2^31 bytes, rejected before any HIP call
+    n, ld = 8192, 1 << 21
+    assert L.gemm_nt_f16f32_plan(n, n, n, 1).decode().startswith("wg256x256")
+    assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, n, n, n, n, n, ld, None) == -1
+    assert "2^31" in L.fp16mc_last_error().decode()
+    assert L.gemm_nt_ex(FAKE, FAKE, FAKE, n, n, n, n, n, 2 * ld, 1, 0, 0, 0, 1, 1, 0, None) == -1
+    assert "2^31" in L.fp16mc_last_error().decode()
+
+
 def test_gemm_batched_validation(L):
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, -1, 0, 0, 0, None) == -1
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 12, 128, 64, None) == -2
