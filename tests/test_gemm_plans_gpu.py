@@ -4,7 +4,10 @@ and two type combinations, against the CPU oracle through the C ABI.
 Each shape below is chosen so that the plan logic picks the named
 configuration (asserted); shapes are ragged in M, N and K.  The large ones
 are checked on sampled rows -- the first and last three rows and 26 random
-ones, every column -- plus all-finite and untouched padding.
+ones, every column -- plus all-finite and untouched padding.  Out is
+followed by GUARD rows of NaN that must stay untouched: the last row tile of
+every shape reaches past M, and the kernels rely on the output buffer's
+range to drop those rows.
 """
 
 import zlib
@@ -33,6 +36,7 @@ PLAN_SHAPES = {
     "wg256x256": (8100, 2000, 4100),
 }
 ORDERS = [("k", "k"), ("k", "mn"), ("mn", "k"), ("mn", "mn")]
+GUARD = 37
 TYPES = [("f16", "f32", False), ("bf16", "bf16", True)]
 
 
@@ -70,13 +74,15 @@ def test_plan(f, plan, a_order, b_order, ab, out_fmt, acc):
     per16 = 4 if out_fmt == "f32" else 8
     ldo = N + 3
     ldo += (-ldo) % per16
-    out = torch.full((M, ldo), float("nan"), dtype=TORCH[out_fmt], device="cuda")
+    buf = torch.full((M + GUARD, ldo), float("nan"), dtype=TORCH[out_fmt], device="cuda")
+    out = buf[:M]
     C = None
     if acc:
         C = torch.from_numpy(inputs.accumulator_f32((M, N), seed=M)).to(TORCH[out_fmt])
         out[:, :N] = C.cuda()
         C = C.double().numpy()
     pad_before = out[:, N:].clone()
+    guard_before = buf[M:].clone()
     a, lda = _stored(A, a_order, ab)
     b, ldb = _stored(B, b_order, ab)
     f.gemm_ex_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldo, 1, 0, 0, 0,
@@ -85,6 +91,7 @@ def test_plan(f, plan, a_order, b_order, ab, out_fmt, acc):
     torch.cuda.synchronize()
     view = torch.int16 if out_fmt != "f32" else torch.int32
     assert torch.equal(out[:, N:].view(view), pad_before.view(view)), "padding of Out written"
+    assert torch.equal(buf[M:].view(view), guard_before.view(view)), "rows past M written"
     assert bool(torch.isfinite(out[:, :N]).all())
     if M <= 64:
         rows = np.arange(M)
