@@ -532,7 +532,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     asm volatile("s_barrier" ::: "memory");
   };
 
-  // ---- Out tile addressing (accumulate prologue and epilogue) -------------------
+  // ---- Out tile addressing (epilogue) ---------------------------------------------
   // Every access to Out is a buffer access relative to the tile's origin,
   // with the whole offset (lane, column block and row) in the per-lane
   // offset register, which the buffer's range check covers.  The buffer ends
