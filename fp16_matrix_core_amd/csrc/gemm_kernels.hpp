@@ -175,7 +175,7 @@ using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
 // workgroup each, non-temporal) against a B that every workgroup shares.
 // 16384x8x16384: 93 us against 118 us for a dedicated register-streaming
 // kernel with 16x16x32 MFMAs (full-line direct loads and the streaming hint
-// make the difference).
+// make the difference), 80 us with the staggered K sweep of the K loop.
 using CfgTall = Cfg<64, 32, 2, 1, 1, 4, 1, 64, 1>;
 // The 128x64 tiles with operands and output streamed, for problems that are
 // one tile each (batches of small products; each workgroup reads and writes
@@ -607,9 +607,23 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   constexpr int kAhead = kS - 1;                   // prefetch distance in slices
   const int64_t nfull = K / C::BK;
   Frags f0, f1;
+  // A streamed operand (each tile's rows read by that workgroup alone) is
+  // swept from a per-workgroup starting slice, wrapping around: its rows lie
+  // a power-of-two stride apart, and with every workgroup at the same K
+  // offset their reads crowd the same memory channels (a 512 MiB row stream
+  // ran at 5.9-6.0 TB/s in lockstep and 6.8-6.9 TB/s with staggered starts;
+  // 16384x8x16384 93 -> 80 us).  Tiles that share operand panels keep the
+  // common order, which their L2 reuse depends on (staggering the 8 XCDs'
+  // starts gained under 1% at 8192^3; a one-tile-wide 128x64 grid gained
+  // 1%).  The order of the sum changes, not its terms.
+  constexpr bool kRotate = (C::STREAM & 3) != 0;
+  const int64_t rot = kRotate && nfull > 1
+                          ? __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blockIdx.x * 37u % static_cast<uint32_t>(nfull)))
+                          : 0;
   auto slice_of = [&](int64_t slice) {
     // slices past the end reload the last one into an idle stage: no branch, never read
-    return slice < nfull ? slice : nfull - 1;
+    const int64_t s = (slice < nfull ? slice : nfull - 1) + rot;
+    return s < nfull ? s : s - nfull;
   };
   std::integral_constant<int, (kAhead - 1) * kLoads> keep_later;
   static_assert((kAhead - 1) * kLoads <= 63, "loads kept in flight must fit the 6-bit vmcnt");
