@@ -250,6 +250,24 @@ def test_skinny_ragged(f, shape):
     assert np.isnan(pad).all()
 
 
+WIDE = [(8, 4097, 1000), (32, 3000, 4100), (1, 777, 333), (17, 2048, 2048), (5, 65, 640)]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "x".join(map(str, s)))
+def test_wide_ragged(f, shape):
+    """M <= 32 shapes on the wide tiles (B streamed): ragged N and K; K spans
+    several slices, so each workgroup's staggered K sweep wraps around, and
+    most end with a partial slice."""
+    M, N, K = shape
+    assert f.plan(M, N, K).startswith("wide32x64")
+    rng = np.random.default_rng(M + 31 * N + 7 * K)
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    got, pad = _run(f, A, B, ldo_pad=4)
+    _assert_parity(got, A, B)
+    assert np.isnan(pad).all()
+
+
 def test_skinny_batched(f):
     rng = np.random.default_rng(61)
     A = inputs.uniform_f16((3, 130, 256), rng)
