@@ -56,6 +56,12 @@ GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool /
   if (M <= 32) return GemmPlan::kWide;
   // a batch of one-tile problems: nothing is read twice
   if (batch > 1 && M <= 128 && N <= 64) return GemmPlan::kWg128x64Stream;
+  // Long-K products with fewer than 64 tiles of 128x64 leave most CUs idle on
+  // the larger tiles; one wavefront per 32x32 tile spreads them over eight
+  // times as many workgroups (512^2 x 16384: 69 -> 54 us, 256^2 x 16384:
+  // 68 -> 52 us, 512^2 x 4096: 20 -> 17 us; with 64 or more such tiles, or
+  // shorter K, the larger tiles tie or win: 1024^2 x 4096 22 vs 27 us).
+  if (K >= 4096 && ((M + 127) / 128) * ((N + 63) / 64) * batch < 64) return GemmPlan::kWave32;
   GemmPlan best = GemmPlan::kWg128x64;
   double best_rate = -1.0;
   for (const TileModel& m : kModels) {

@@ -250,6 +250,23 @@ def test_skinny_ragged(f, shape):
     assert np.isnan(pad).all()
 
 
+LONG_K = [(512, 512, 16384), (300, 500, 4100), (100, 200, 8200), (256, 1000, 4096)]
+
+
+@pytest.mark.parametrize("shape", LONG_K, ids=lambda s: "x".join(map(str, s)))
+def test_long_k_small_output(f, shape):
+    """Long K with fewer than 64 tiles of 128x64: one wavefront per 32x32 tile
+    (ragged M, N and K); every element checked."""
+    M, N, K = shape
+    assert f.plan(M, N, K).startswith("wave32x32")
+    rng = np.random.default_rng(M + 31 * N + 7 * K)
+    A = inputs.uniform_f16((M, K), rng)
+    B = inputs.uniform_f16((N, K), rng)
+    got, pad = _run(f, A, B, ldo_pad=4)
+    _assert_parity(got, A, B)
+    assert np.isnan(pad).all()
+
+
 WIDE = [(8, 4097, 1000), (32, 3000, 4100), (1, 777, 333), (17, 2048, 2048), (5, 65, 640)]
 
 
