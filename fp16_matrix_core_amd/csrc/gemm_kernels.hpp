@@ -149,6 +149,14 @@ struct Cfg {
 };
 
 using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
+// The same tile with 64-wide K slices, for products with K >= 1024 too small
+// to fill the chip with larger tiles: whole 128-byte rows per direct load
+// (512^2 x 16384: 53 -> 40 us against 32-wide slices), and tiles grouped in
+// strips of 8 rows so that an XCD's tiles share operand panels in its L2
+// (256 x 2048 x 8192: 39 -> 24 us against ungrouped rows).  Tiny problems
+// keep the 32-wide slices, which cost less latency when K fits one slice
+// (16x8x16: 4.0 against 6.3 us).
+using CfgWave32Long = Cfg<32, 32, 1, 1, 8, 4, 1, 64>;
 // 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
 // by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
 // As for every large-tile configuration below, K-contiguous operands use
@@ -923,6 +931,7 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
     case GemmPlan::kWg256x128: return launch_by_order<CfgWg256x128, CfgWg256x128Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x128: return launch_by_order<CfgWg128x128, CfgWg128x128Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kWide: return launch_cfg<CfgWide, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWave32Long: return launch_cfg<CfgWave32Long, A_MN, B_MN>(p, stream);
     default: return hipSuccess;
   }
 }

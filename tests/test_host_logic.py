@@ -197,12 +197,13 @@ def test_plans(L):
     import fp16_matrix_core_amd as f
     assert f.plan(0, 8, 8) is None
     assert f.plan(16, 8, 16).startswith("wave32x32")
-    # long K with fewer than 64 tiles of 128x64: one wavefront per 32x32 tile
-    assert f.plan(512, 512, 16384).startswith("wave32x32")
-    assert f.plan(256, 1000, 4096).startswith("wave32x32")
-    assert f.plan(512, 512, 4095).startswith("wg128x64_")
+    # K >= 1024 and at most 768 tiles of 32x32: one wavefront per tile, 64-wide K slices
+    assert f.plan(512, 512, 16384) == "wave32x32k64_mfma32x32x16"
+    assert f.plan(256, 2048, 8192).startswith("wave32x32k64_")
+    assert f.plan(768, 1024, 1024).startswith("wave32x32k64_")
+    assert f.plan(768, 1056, 1024).startswith("wg128x64_")
+    assert f.plan(512, 512, 1023).startswith("wg128x64_")
     assert f.plan(1024, 1024, 4096).startswith("wg128x64_")
-    assert f.plan(512, 1024, 8192).startswith("wg128x64_")
     assert f.plan(128, 64, 64).startswith("wg128x64_")
     assert f.plan(128, 64, 64, 4096).startswith("wg128x64s_")      # one-tile problems: streamed
     assert f.plan(129, 64, 64, 4096).startswith("wg128x64_")
