@@ -149,14 +149,16 @@ struct Cfg {
 };
 
 using CfgWave32 = Cfg<32, 32, 1, 1, 1, 4, 1>;
-// The same tile with 64-wide K slices, for products with K >= 1024 too small
-// to fill the chip with larger tiles: whole 128-byte rows per direct load
-// (512^2 x 16384: 53 -> 40 us against 32-wide slices), and tiles grouped in
-// strips of 8 rows so that an XCD's tiles share operand panels in its L2
-// (256 x 2048 x 8192: 39 -> 24 us against ungrouped rows).  Tiny problems
-// keep the 32-wide slices, which cost less latency when K fits one slice
-// (16x8x16: 4.0 against 6.3 us).
-using CfgWave32Long = Cfg<32, 32, 1, 1, 8, 4, 1, 64>;
+// 64x64 tiles, four wavefronts of 32x32 (64-wide slices in four 16 KiB
+// stages), for products with at most 256 such tiles -- at most one per CU --
+// that the larger tiles would spread over a fraction of the CUs.  Against
+// 128x64 tiles: 1024^2 x 4096 22 -> 15 us, 1024^2 x 8192 38 -> 24 us,
+// 512^2 x 16384 69 -> 42 us, 2048 x 512 x 4096 21 -> 15 us; with more tiles
+// the 128x64 ones win again (1280^2 x 4096 24.5 against 22 us).  One
+// wavefront per 32x32 tile with 64-wide slices was within 5% of these on
+// long-K shapes and up to 16% slower on others.
+using CfgWg64 = Cfg<64, 64, 2, 2, 8, 4, 1, 64, 0, 16>;
+using CfgWg64Mn = Cfg<64, 64, 2, 2, 8, 4, 1, 64>;
 // 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
 // by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
 // As for every large-tile configuration below, K-contiguous operands use
@@ -931,7 +933,7 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
     case GemmPlan::kWg256x128: return launch_by_order<CfgWg256x128, CfgWg256x128Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x128: return launch_by_order<CfgWg128x128, CfgWg128x128Mn, A_MN, B_MN>(p, stream);
     case GemmPlan::kWide: return launch_cfg<CfgWide, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWave32Long: return launch_cfg<CfgWave32Long, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg64: return launch_by_order<CfgWg64, CfgWg64Mn, A_MN, B_MN>(p, stream);
     default: return hipSuccess;
   }
 }

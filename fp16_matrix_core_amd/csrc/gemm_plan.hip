@@ -56,14 +56,10 @@ GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool /
   if (M <= 32) return GemmPlan::kWide;
   // a batch of one-tile problems: nothing is read twice
   if (batch > 1 && M <= 128 && N <= 64) return GemmPlan::kWg128x64Stream;
-  // Products with K >= 1024 and at most 768 tiles of 32x32 leave most CUs
-  // idle on the larger tiles; one wavefront per 32x32 tile spreads them over
-  // up to eight times as many workgroups (against 128x64 tiles: 512^2 x
-  // 16384 69 -> 41 us, 512 x 1024 x 8192 36 -> 23 us, 256 x 2048 x 8192
-  // 33 -> 24 us, 768^2 x 8192 36 -> 29 us, 512^2 x 2048 9.4 -> 7.5 us; at
-  // 1024 such tiles the two tie, 1024^2 x 4096, and beyond the larger tiles
-  // win, 2048^2 x 4096 41 against 88 us).
-  if (K >= 1024 && ((M + 31) / 32) * ((N + 31) / 32) * batch <= 768) return GemmPlan::kWave32Long;
+  // At most 256 tiles of 64x64 (K >= 512): the larger tiles would occupy a
+  // fraction of the CUs; 64x64 tiles give each CU at most one (1024^2 x 4096
+  // 22 -> 15 us, 768^2 x 2048 9.8 -> 7.0 us, 512^2 x 16384 69 -> 42 us).
+  if (K >= 512 && ((M + 63) / 64) * ((N + 63) / 64) * batch <= 256) return GemmPlan::kWg64;
   GemmPlan best = GemmPlan::kWg128x64;
   double best_rate = -1.0;
   for (const TileModel& m : kModels) {
@@ -87,7 +83,7 @@ const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn) {
     case GemmPlan::kWg256x128: return mn ? "wg256x128_w4_mfma32x32x16" : "wg256x128_w4_mfma16x16x32";
     case GemmPlan::kWg128x128: return mn ? "wg128x128_w4_mfma32x32x16" : "wg128x128_w4_mfma16x16x32";
     case GemmPlan::kWide: return "wide32x64_w2_mfma32x32x16";
-    case GemmPlan::kWave32Long: return "wave32x32k64_mfma32x32x16";
+    case GemmPlan::kWg64: return mn ? "wg64x64_w4_mfma32x32x16" : "wg64x64_w4_mfma16x16x32";
     default: return nullptr;
   }
 }
@@ -103,7 +99,7 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
     case GemmPlan::kWg256x128: return tiles_of<CfgWg256x128>(M, N, batch, &tm, &tn);
     case GemmPlan::kWg128x128: return tiles_of<CfgWg128x128>(M, N, batch, &tm, &tn);
     case GemmPlan::kWide: return tiles_of<CfgWide>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWave32Long: return tiles_of<CfgWave32Long>(M, N, batch, &tm, &tn);
+    case GemmPlan::kWg64: return tiles_of<CfgWg64>(M, N, batch, &tm, &tn);
     default: return 0;
   }
 }
@@ -132,7 +128,7 @@ bool gemm_plan_fits_offsets(GemmPlan plan, int64_t K, int64_t lda, int64_t ldb, 
     case GemmPlan::kWg256x128: return fits_offsets<CfgWg256x128>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
     case GemmPlan::kWg128x128: return fits_offsets<CfgWg128x128>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
     case GemmPlan::kWide: return fits_offsets<CfgWide>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
-    case GemmPlan::kWave32Long: return fits_offsets<CfgWave32Long>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
+    case GemmPlan::kWg64: return fits_offsets<CfgWg64>(K, lda, ldb, ldo, out_bytes, a_mn, b_mn);
     default: return true;
   }
 }

@@ -40,7 +40,7 @@ enum class GemmPlan : int {
   kWg256x128 = 6,       // 4 wavefronts per 256x128 tile
   kWg128x128 = 7,       // 4 wavefronts per 128x128 tile, two workgroups per CU
   kWide = 8,            // M <= 32: 2 wavefronts per 32x64 tile, B streamed
-  kWave32Long = 9,      // long K, few tiles: one wavefront per 32x32 tile, 64-wide K slices
+  kWg64 = 9,            // 4 wavefronts per 64x64 tile (at most one tile per CU)
 };
 
 GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool a_mn, bool b_mn);

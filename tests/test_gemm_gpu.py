@@ -250,15 +250,15 @@ def test_skinny_ragged(f, shape):
     assert np.isnan(pad).all()
 
 
-LONG_K = [(512, 512, 16384), (300, 500, 4100), (100, 200, 8200), (256, 1000, 4096), (200, 1500, 1030), (40, 3000, 2000)]
+SMALL_GRID = [(512, 512, 16384), (300, 500, 4100), (100, 200, 8200), (256, 1000, 4096), (1000, 1000, 600), (40, 3000, 2000)]
 
 
-@pytest.mark.parametrize("shape", LONG_K, ids=lambda s: "x".join(map(str, s)))
-def test_long_k_small_output(f, shape):
-    """K >= 1024 with at most 768 tiles of 32x32: one wavefront per tile, 64-wide
-    K slices (ragged M, N and K); every element checked."""
+@pytest.mark.parametrize("shape", SMALL_GRID, ids=lambda s: "x".join(map(str, s)))
+def test_small_grid_64x64_tiles(f, shape):
+    """K >= 512 with at most 256 tiles of 64x64: at most one tile per CU
+    (ragged M, N and K); every element checked."""
     M, N, K = shape
-    assert f.plan(M, N, K).startswith("wave32x32k64_")
+    assert f.plan(M, N, K).startswith("wg64x64_")
     rng = np.random.default_rng(M + 31 * N + 7 * K)
     A = inputs.uniform_f16((M, K), rng)
     B = inputs.uniform_f16((N, K), rng)

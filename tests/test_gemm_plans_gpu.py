@@ -28,7 +28,7 @@ NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
 
 PLAN_SHAPES = {
     "wave32x32": (31, 29, 70),
-    "wave32x32k64": (300, 500, 4100),
+    "wg64x64": (300, 500, 4100),
     "tall64x32": (1000, 17, 300),
     "wide32x64": (20, 1000, 77),
     "wg128x64": (300, 520, 200),

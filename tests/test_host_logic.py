@@ -197,13 +197,13 @@ def test_plans(L):
     import fp16_matrix_core_amd as f
     assert f.plan(0, 8, 8) is None
     assert f.plan(16, 8, 16).startswith("wave32x32")
-    # K >= 1024 and at most 768 tiles of 32x32: one wavefront per tile, 64-wide K slices
-    assert f.plan(512, 512, 16384) == "wave32x32k64_mfma32x32x16"
-    assert f.plan(256, 2048, 8192).startswith("wave32x32k64_")
-    assert f.plan(768, 1024, 1024).startswith("wave32x32k64_")
-    assert f.plan(768, 1056, 1024).startswith("wg128x64_")
-    assert f.plan(512, 512, 1023).startswith("wg128x64_")
-    assert f.plan(1024, 1024, 4096).startswith("wg128x64_")
+    # K >= 512 and at most 256 tiles of 64x64: at most one 64x64 tile per CU
+    assert f.plan(512, 512, 16384) == "wg64x64_w4_mfma16x16x32"
+    assert f.plan(1024, 1024, 4096).startswith("wg64x64_")
+    assert f.plan(1024, 1024, 512).startswith("wg64x64_")
+    assert f.plan(1024, 1088, 4096).startswith("wg128x64_")
+    assert f.plan(1024, 1024, 511).startswith("wg128x64_")
+    assert f.plan_ex(1024, 1024, 4096, 1, 1, 0) == "wg64x64_w4_mfma32x32x16"
     assert f.plan(128, 64, 64).startswith("wg128x64_")
     assert f.plan(128, 64, 64, 4096).startswith("wg128x64s_")      # one-tile problems: streamed
     assert f.plan(129, 64, 64, 4096).startswith("wg128x64_")
@@ -213,7 +213,8 @@ def test_plans(L):
     assert f.plan(3000, 5000, 704).startswith("wg128x128")
     assert f.plan(12288, 12288, 1024).startswith("wg256x256")  # many waves of tiles: largest tiles
     assert f.plan(2048, 2048, 2048).startswith("wg128x64_")
-    assert f.plan(16384, 64, 4096).startswith("wg128x64_")     # 256-wide tiles would be 3/4 empty
+    assert f.plan(16384, 64, 4096).startswith("wg64x64_")      # 256 tiles of 64x64: one per CU
+    assert f.plan(16384, 128, 4096).startswith("wg128x64_")    # 512 of them: the larger tiles win again
     assert f.plan(8, 16384, 16384).startswith("wide32x64")
     assert f.plan(16384, 8, 16384).startswith("tall64x32")
     assert f.plan(100, 32, 64).startswith("tall64x32")
