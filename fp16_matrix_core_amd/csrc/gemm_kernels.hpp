@@ -32,7 +32,8 @@
 //                   fragments of the next K step are read while the current
 //                   one multiplies; one workgroup barrier per slice.
 //   scheduler       XCD-contiguous ranges of tile ids, grouped so that the
-//                   tiles an XCD runs together share A and B panels in L2.
+//                   tiles an XCD runs together share A and B panels in L2
+//                   (streamed operands: dispatch order, K staggered).
 //   edges           rows past M or N are clamped on load (their results are
 //                   never stored); K past the end is zero-filled; Out is
 //                   accessed through a buffer that ends at the tile's last
@@ -315,7 +316,13 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   const int wn = wave % C::WN;
 
   // ---- tile scheduler -------------------------------------------------------
-  const uint32_t lin = sched::xcd_remap(blockIdx.x, static_cast<uint32_t>(total));
+  // Tiles that share operand panels take XCD-contiguous id ranges (their L2
+  // reuse); with a streamed operand nothing worth keeping is shared, and the
+  // dispatch order itself keeps the concurrently running tiles on adjacent
+  // memory (the ranges put the 8 XCDs' streams a power-of-two stride apart:
+  // 4096 x 128x64x64 43 -> 41 us, 32x16384x8192 43 -> 40 us).
+  const uint32_t lin =
+      (C::STREAM & 3) != 0 ? blockIdx.x : sched::xcd_remap(blockIdx.x, static_cast<uint32_t>(total));
   const uint32_t per_problem = static_cast<uint32_t>(tiles_m * tiles_n);
   const uint32_t b = __builtin_amdgcn_readfirstlane(lin / per_problem);
   const sched::Tile tile = sched::grouped_tile(lin - b * per_problem, static_cast<uint32_t>(tiles_m),
