@@ -59,7 +59,7 @@ GemmPlan choose_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t batch, bool /
   // At most 256 tiles of 64x64 (K >= 512): the larger tiles would occupy a
   // fraction of the CUs; 64x64 tiles give each CU at most one (1024^2 x 4096
   // 22 -> 15 us, 768^2 x 2048 9.8 -> 7.0 us, 512^2 x 16384 69 -> 42 us).
-  if (K >= 512 && ((M + 63) / 64) * ((N + 63) / 64) * batch <= 256) return GemmPlan::kWg64;
+  if (K >= 512 && double((M + 63) / 64) * double((N + 63) / 64) * double(batch) <= 256.0) return GemmPlan::kWg64;
   GemmPlan best = GemmPlan::kWg128x64;
   double best_rate = -1.0;
   for (const TileModel& m : kModels) {
