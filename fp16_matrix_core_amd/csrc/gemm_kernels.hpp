@@ -207,14 +207,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
-// Elements [k, k+8) of a row, zero past K.  `row` points at element 0.
-// Only the last, partial K slice of a problem takes this path.
+// Elements [k, k+8) of a row, zero past K.  `row` points at element 0 and
+// k is a multiple of 8, so a chunk wholly inside the row is one aligned
+// 16-byte load (rows are 16-byte aligned); only the chunk that straddles K
+// goes element by element.  Only the last, partial K slice of a problem
+// takes this path.
 __device__ __forceinline__ u32x4 load_chunk_masked(const unsigned short* row, int64_t k, int64_t K) {
-  const unsigned short* r16 = row;
+  if (k + 8 <= K) return *reinterpret_cast<const u32x4*>(row + k);
   unsigned int w[4] = {0u, 0u, 0u, 0u};
+  if (k < K) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (k + e < K) w[e >> 1] |= static_cast<unsigned int>(r16[k + e]) << (16 * (e & 1));
+    for (int e = 0; e < 8; ++e) {
+      if (k + e < K) w[e >> 1] |= static_cast<unsigned int>(row[k + e]) << (16 * (e & 1));
+    }
   }
   return u32x4{w[0], w[1], w[2], w[3]};
 }
