@@ -294,3 +294,18 @@ def test_skinny_batched(f):
     ref, bound = oracle.gemm_nt_batched(A, B)
     ok, worst, n_bad = oracle.within_bound(out.cpu().numpy(), ref, bound)
     assert ok, f"{n_bad} bad, worst {worst:.3g}"
+
+
+def test_small_grid_batched(f):
+    """A batch on the 64x64 tiles (3 problems of 300x200x1000: 60 tiles in all)
+    and on the wide tiles (M <= 32), each problem checked."""
+    rng = np.random.default_rng(62)
+    for (P, M, N, K), plan in (((3, 300, 200, 1000), "wg64x64_"), ((2, 20, 700, 640), "wide32x64_")):
+        assert f.plan(M, N, K, P).startswith(plan)
+        A = inputs.uniform_f16((P, M, K), rng)
+        B = inputs.uniform_f16((P, N, K), rng)
+        out = f.gemm_nt_batched(_dev(A), _dev(B))
+        torch.cuda.synchronize()
+        ref, bound = oracle.gemm_nt_batched(A, B)
+        ok, worst, n_bad = oracle.within_bound(out.cpu().numpy(), ref, bound)
+        assert ok, f"{plan} batch: {n_bad} bad, worst {worst:.3g}"
