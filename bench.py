@@ -15,11 +15,19 @@ Besides the headline, the same line carries:
                 summary matches the current kernel source;
   cpu_baseline  the CPU oracle (numpy float64) on a bounded row sample of the
                 same workload, timed on this host;
+  step_us       every timed launch's own duration (HIP events between the
+                launches), so that a clock still ramping up under a short
+                warm-up shows in the record;
   secondary     frag_copy (2^20 tiles, every num / layout / direction) in GB/s
-                against HBM bandwidth with rotating buffers, the batched
-                4096 x (128x64x64) product, the 16384x8x16384 skinny product,
-                the single 16x8x16 tile and 128x64x64 workgroup (us per call),
-                and the 8192^3 launch with other types and storage orders.
+                against HBM bandwidth, cold (three rotating buffer sets, more
+                than the 256 MB last-level cache holds) and warm (one set
+                reused), the batched 4096 x (128x64x64) product and the
+                16384x8x16384 skinny product (cold and warm), the single
+                16x8x16 tile and 128x64x64 workgroup (us per call), the
+                8192^3 launch with other types and storage orders, and two
+                ceilings from bench_ceiling.hip: the MFMA pipe alone on the
+                workload's operand values and on zeros, and a plain copy of
+                frag_copy's size.
 """
 
 import argparse
@@ -40,6 +48,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 GEMM_SOURCES = ["fp16_matrix_core_amd/csrc/gemm_kernels.hpp", "fp16_matrix_core_amd/csrc/gemm_nt.hip",
                 "fp16_matrix_core_amd/csrc/layout.hpp", "fp16_matrix_core_amd/csrc/kernels.hpp"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.txt")
+CEILING_LIB = os.path.join(ROOT, "libbench_ceiling.so")
 
 
 def log(*a):
@@ -121,7 +130,11 @@ def cpu_baseline(A, B, target_s=10.0):
 
 
 def bench_frag(torch, f, stream, reps=20, sets=3):
-    """frag_copy GB/s over 2^20 tiles (256 MiB moved per call), rotating buffer sets."""
+    """frag_copy GB/s over 2^20 tiles (256 MiB moved per call).
+
+    cold: three rotating buffer sets (768 MiB, more than the last-level cache
+    holds, so every call streams from HBM); warm: one set called repeatedly.
+    """
     from fp16_matrix_core_amd import inputs
     n_tiles = inputs.FRAG_TILES
     nbytes = n_tiles * 128
@@ -129,25 +142,27 @@ def bench_frag(torch, f, stream, reps=20, sets=3):
     srcs = [bits.clone() for _ in range(sets)]
     dsts = [torch.empty_like(bits) for _ in range(sets)]
     timer = StreamTimer(torch, stream)
-    out = {}
+    cold, warm = {}, {}
     for num in (1, 2, 4):
         for col in (0, 1):
             for direction, dname in ((0, "load"), (1, "store"), (2, "roundtrip")):
-                i = [0]
+                name = f"num{num}_{'col' if col else 'row'}_{dname}"
+                for res, nsets in ((cold, sets), (warm, 1)):
+                    i = [0]
 
-                def call():
-                    k = i[0] % sets
-                    i[0] += 1
-                    f.frag_copy_raw(srcs[k].data_ptr(), dsts[k].data_ptr(), n_tiles, num, col, direction,
-                                    stream.cuda_stream)
-                for _ in range(3):
-                    call()
-                ms = timer.time(call, reps)
-                out[f"num{num}_{'col' if col else 'row'}_{dname}"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
-    vals = list(out.values())
+                    def call():
+                        k = i[0] % nsets
+                        i[0] += 1
+                        f.frag_copy_raw(srcs[k].data_ptr(), dsts[k].data_ptr(), n_tiles, num, col, direction,
+                                        stream.cuda_stream)
+                    for _ in range(3):
+                        call()
+                    ms = timer.time(call, reps)
+                    res[name] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    vals = list(cold.values())
     return {"unit": "GB/s", "bytes_per_call": 2 * nbytes, "peak": PEAK_HBM_GBS,
             "min_frac": round(min(vals) / PEAK_HBM_GBS, 4), "max_frac": round(max(vals) / PEAK_HBM_GBS, 4),
-            "results": out}
+            "results": cold, "warm": warm}
 
 
 def bench_batched(torch, f, stream, reps=20):
@@ -165,10 +180,18 @@ def bench_batched(torch, f, stream, reps=20):
     for _ in range(3):
         call()
     ms = StreamTimer(torch, stream).time(call, reps)
+
+    def warm_call():
+        f.gemm_nt_batched(*sets[0])
+    for _ in range(3):
+        warm_call()
+    ms_warm = StreamTimer(torch, stream).time(warm_call, reps)
     flop = 2.0 * 4096 * 128 * 64 * 64
     nbytes = 4096 * (128 * 64 * 2 + 64 * 64 * 2 + 128 * 64 * 4)
     return {"plan": f.plan(128, 64, 64, 4096), "us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 2),
-            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "warm_us": round(ms_warm * 1e3, 2), "warm_GB/s": round(nbytes / ms_warm / 1e6, 1),
+            "timing": "us/GB/s: three rotating buffer sets (705 MB, streamed from HBM); warm_*: one set reused"}
 
 
 def bench_skinny(torch, f, stream, reps=20):
@@ -186,10 +209,18 @@ def bench_skinny(torch, f, stream, reps=20):
     for _ in range(3):
         call()
     ms = StreamTimer(torch, stream).time(call, reps)
+
+    def warm_call():
+        f.gemm_nt(*sets[0])
+    for _ in range(3):
+        warm_call()
+    ms_warm = StreamTimer(torch, stream).time(warm_call, reps)
     flop = 2.0 * 16384 * 8 * 16384
     nbytes = 16384 * 16384 * 2 + 8 * 16384 * 2 + 16384 * 8 * 4
     return {"plan": f.plan(16384, 8, 16384), "us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 2),
-            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+            "GB/s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "warm_us": round(ms_warm * 1e3, 2), "warm_GB/s": round(nbytes / ms_warm / 1e6, 1),
+            "timing": "us/GB/s: two alternating buffer sets (1.08 GB); warm_*: one set (538 MB) reused"}
 
 
 def bench_small(torch, f, stream, reps=200):
@@ -269,8 +300,64 @@ def bench_layouts(torch, f, stream, A, B, reps=20):
     return res
 
 
+def ceiling_lib():
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(CEILING_LIB)
+    L.ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
+    L.ceiling_mfma.restype = ctypes.c_int
+    L.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.ceiling_copy.restype = ctypes.c_int
+    return L
+
+
+def bench_ceilings(torch, stream, a, reps=10):
+    """MFMA-only loops (one workgroup of 4 wavefronts per CU, 256 accumulators per
+    lane) on the 8192^3 workload's A values and on zeros; a plain copy of the
+    2^28 bytes a fragment copy moves (three rotating sets)."""
+    L = ceiling_lib()
+    sp = stream.cuda_stream
+    grid = 256
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    ops = {"workload": a.reshape(-1), "zeros": torch.zeros_like(a.reshape(-1))}
+    timer = StreamTimer(torch, stream)
+    res = {"unit": "TFLOP/s", "grid": grid}
+    for mi, iters in ((16, 4096), (32, 2048)):
+        flop = 2.0 * grid * 4 * iters * (64 * 16 * 16 * 32 if mi == 16 else 16 * 32 * 32 * 16)
+        for name, buf in ops.items():
+            nb = buf.numel() * buf.element_size()
+
+            def call():
+                rc = L.ceiling_mfma(buf.data_ptr(), nb, sink.data_ptr(), mi, iters, grid, sp)
+                if rc != 0:
+                    raise RuntimeError(f"ceiling_mfma failed ({rc})")
+            for _ in range(5):
+                call()
+            ms = timer.time(call, reps)
+            res[f"mfma{mi}x{mi}_{name}"] = round(flop / ms / 1e9, 1)
+    nbytes = 1 << 27                    # 128 MiB read + 128 MiB written per call
+    bufs = [(torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0),
+             torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")) for _ in range(3)]
+    i = [0]
+
+    def copy():
+        s_, d_ = bufs[i[0] % 3]
+        i[0] += 1
+        if L.ceiling_copy(s_.data_ptr(), d_.data_ptr(), nbytes, sp) != 0:
+            raise RuntimeError("ceiling_copy failed")
+    for _ in range(5):
+        copy()
+    ms = timer.time(copy, 20)
+    res["copy_2^28B_GB/s"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    return res
+
+
 def pmc_pass(torch, f):
-    """Three 8192^3 launches, then three copies of 1 GiB (the counter calibration kernel)."""
+    """A short program for rocprofv3 counter passes: three 8192^3 launches, three
+    copies of 1 GiB (the counter calibration), two MFMA-only loops on the
+    workload's values, and one call of each frag_copy variant (2^20 tiles)."""
     from fp16_matrix_core_amd import inputs
     A, B = inputs.large_square()
     a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
@@ -283,7 +370,35 @@ def pmc_pass(torch, f):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("pmc pass done: 3 x gemm_nt 8192^3, 3 x copy of 1 GiB")
+    L = ceiling_lib()
+    sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    flat = a.reshape(-1)
+    for _ in range(2):
+        if L.ceiling_mfma(flat.data_ptr(), flat.numel() * 2, sink.data_ptr(), 16, 4096, 256, sp) != 0:
+            raise RuntimeError("ceiling_mfma failed")
+    torch.cuda.synchronize()
+    del src, dst
+    n_tiles = inputs.FRAG_TILES
+    img = torch.from_numpy(inputs.frag_bits().view(np.int16)).cuda()
+    frag = torch.empty_like(img)
+    for num in (1, 2, 4):
+        for col in (0, 1):
+            for direction in (0, 1, 2):
+                f.frag_copy_raw(img.data_ptr(), frag.data_ptr(), n_tiles, num, col, direction, sp)
+    torch.cuda.synchronize()
+    log("pmc pass done: 3 x gemm_nt 8192^3, 3 x copy of 1 GiB, 2 x MFMA loop, 18 x frag_copy")
+
+
+def run_secondary(torch, f, stream, a, b, A, B):
+    log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders")
+    return {"ceilings": bench_ceilings(torch, stream, a),
+            "frag_copy": bench_frag(torch, f, stream),
+            "batched_4096x128x64x64": bench_batched(torch, f, stream),
+            "skinny_16384x8x16384": bench_skinny(torch, f, stream),
+            "small": bench_small(torch, f, stream),
+            "gemm_8192_types": bench_types(torch, f, stream, a, b),
+            "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
 
 
 def main():
@@ -294,6 +409,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--headline-first", action="store_true",
+                    help="time the headline before the secondary measurements (default: after them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the product is not sharded "
@@ -323,27 +440,37 @@ def main():
     def step():
         f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, K, K, N, sp)
 
+    secondary = None
+    if not args.no_secondary and not args.headline_first:
+        secondary = run_secondary(torch, f, stream, a, b, A, B)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # One event before each timed launch and one after the last: the total
+    # gives the average launch time, the differences each launch's own.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    events[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_event = start.elapsed_time(end) / args.steps
+    step_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    ms_event = events[0].elapsed_time(events[-1]) / args.steps
     ms_step = wall * 1e3 / args.steps
     flop = 2.0 * M * N * K
     tflops = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (ms_event * 1e-3) / 1e12
     log(f"{plan}: {ms_event * 1e3:.1f} us/launch (events), {achieved:.1f} TFLOP/s")
 
+    if not args.no_secondary and args.headline_first:
+        secondary = run_secondary(torch, f, stream, a, b, A, B)
+
     khash = gemm_source_hash()
     traffic = read_traffic(khash)
+    srt = sorted(step_ms)
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -354,16 +481,21 @@ def main():
         "pct_of_peak": round(100 * achieved / PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_kind": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB "
+                                     "copy); reads served by the 256 MB last-level cache count too",
                      "kernel": plan, "us_per_launch": round(ms_event * 1e3, 2), "source_hash": khash},
+        "step_us": {"min": round(srt[0] * 1e3, 1), "median": round(srt[len(srt) // 2] * 1e3, 1),
+                    "max": round(srt[-1] * 1e3, 1),
+                    "each": [round(x * 1e3, 1) for x in step_ms] if len(step_ms) <= 50 else None},
+        "order": "headline first" if args.headline_first or args.no_secondary else
+                 "secondary measurements first, then the headline's warm-up and timed launches",
     }
-    if not args.no_secondary:
-        log("secondary: frag_copy, batched, skinny, operand/output types, storage orders")
-        result["secondary"] = {"frag_copy": bench_frag(torch, f, stream),
-                               "batched_4096x128x64x64": bench_batched(torch, f, stream),
-                               "skinny_16384x8x16384": bench_skinny(torch, f, stream),
-                               "small": bench_small(torch, f, stream),
-                               "gemm_8192_types": bench_types(torch, f, stream, a, b),
-                               "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
+    if secondary is not None:
+        result["secondary"] = secondary
+        ceil = secondary.get("ceilings", {}).get("mfma16x16_workload")
+        if ceil:
+            result["roofline"]["mfma_only_ceiling"] = ceil
+            result["roofline"]["frac_of_mfma_only_ceiling"] = round(achieved / ceil, 4)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(A, B)

@@ -1,0 +1,124 @@
+// bench_ceiling.hip -- two ceilings that bench.py reports beside the product's
+// figures (measurement only; not part of libfp16mc.so):
+//
+//   ceiling_mfma  what the matrix pipe sustains on its own: each wavefront
+//                 loads one set of operand fragments and then issues nothing
+//                 but independent MFMAs on them, into the same 256 fp32
+//                 accumulators per lane that the 256x256 product tile uses
+//                 (8x8 tiles of 16x16x32, or 4x4 tiles of 32x32x16).  No LDS
+//                 and no memory traffic inside the loop.  Fed with the
+//                 product's own operand values it shows how far the operand
+//                 data alone pulls the clock down (the chip is power-limited
+//                 with random operands); fed with zeros, the issue-rate peak.
+//   ceiling_copy  a plain 16-byte copy with non-temporal loads and stores:
+//                 what the memory system gives a pure streaming kernel of
+//                 the same size as a fragment copy.
+//
+// One workgroup of four wavefronts per CU for the MFMA loop (a 256-register
+// accumulator leaves room for one wavefront per SIMD).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int MI>
+struct Shape;
+template <>
+struct Shape<16> {
+  static constexpr int T = 8;   // 8x8 tiles of 16x16 = a 128x128 wave tile
+  typedef f32x4 Acc;
+  static __device__ __forceinline__ Acc mma(f16x8 a, f16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Shape<32> {
+  static constexpr int T = 4;   // 4x4 tiles of 32x32 = a 128x128 wave tile
+  typedef f32x16 Acc;
+  static __device__ __forceinline__ Acc mma(f16x8 a, f16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Wavefront w reads fragments 2T*w .. 2T*w + 2T-1 (16 bytes per lane each):
+// T for the first operand, T for the second.
+template <int MI>
+__global__ void __launch_bounds__(256, 1) mfma_loop(const f16x8* __restrict__ ops, float* __restrict__ sink,
+                                                    int iters) {
+  using S = Shape<MI>;
+  constexpr int T = S::T;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  f16x8 a[T], b[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    a[t] = ops[(static_cast<int64_t>(w) * 2 * T + t) * 64 + lane];
+    b[t] = ops[(static_cast<int64_t>(w) * 2 * T + T + t) * 64 + lane];
+  }
+  typename S::Acc acc[T][T];
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+#pragma unroll
+    for (int j = 0; j < T; ++j) acc[i][j] = typename S::Acc{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+#pragma unroll
+      for (int j = 0; j < T; ++j) acc[i][j] = S::mma(a[i], b[j], acc[i][j]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int v = 0; v < static_cast<int>(sizeof(typename S::Acc) / 4); ++v) s += acc[i][j][v];
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// Each thread copies 4 chunks of 16 bytes, 256 chunks apart (whole 4 KiB per
+// workgroup and step); n16 is a multiple of 1024.
+__global__ void __launch_bounds__(256) copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                              int64_t n16) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(src + base + 256 * k);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v[k], dst + base + 256 * k);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Operand buffer of ops_bytes: 16 KiB per wavefront with 16x16 tiles, 8 KiB
+// with 32x32 (grid * 4 wavefronts); sink: grid * 256 floats.  Returns 0, -1
+// for bad arguments (nothing launched) or a HIP error.
+int ceiling_mfma(const void* ops, int64_t ops_bytes, float* sink, int mi, int iters, int grid, void* stream) {
+  if (grid <= 0 || iters <= 0 || (mi != 16 && mi != 32)) return -1;
+  if (ops_bytes < static_cast<int64_t>(grid) * 4 * (mi == 16 ? 16384 : 8192)) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mi == 16)
+    hipLaunchKernelGGL(mfma_loop<16>, dim3(grid), dim3(256), 0, s, static_cast<const f16x8*>(ops), sink, iters);
+  else
+    hipLaunchKernelGGL(mfma_loop<32>, dim3(grid), dim3(256), 0, s, static_cast<const f16x8*>(ops), sink, iters);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Copies `bytes` (a multiple of 16 KiB) from src to dst, both 16-byte aligned.
+int ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes <= 0 || bytes % 16384 != 0) return -1;
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(copy16, dim3(static_cast<unsigned>(n16 / 1024)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"

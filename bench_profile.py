@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python -m fp16_matrix_core_amd.profiling stats   --csv KERNEL_STATS.csv --match SUBSTR --command CMD --out FILE
-    python -m fp16_matrix_core_amd.profiling traffic --fetch FETCH.csv --write WRITE.csv --match SUBSTR
+    python bench_profile.py stats   --csv KERNEL_STATS.csv --match SUBSTR --command CMD --out FILE
+    python bench_profile.py traffic --fetch FETCH.csv --write WRITE.csv --match SUBSTR
                                                      --command CMD --out FILE
 
 ``stats`` condenses a ``--kernel-trace --stats`` kernel_stats.csv to the

@@ -82,6 +82,19 @@ def _check(status):
         raise Fp16mcError(status, lib().fp16mc_last_error().decode())
 
 
+def _require_device(ref, **tensors):
+    """Every tensor must live on the GPU that holds ``ref``.
+
+    The kernels take raw addresses: a host tensor's address handed to them
+    would fault on the device instead of raising here.
+    """
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the operands on {ref.device}")
+
+
 def _stream_ptr(t):
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -143,6 +156,7 @@ def gemm_nt(a, b, out=None, accumulate=False, out_dtype=None):
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form A @ B.T")
     M, K = a.shape
     N = b.shape[0]
+    _require_device(a, a=a, b=b)
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs an existing out")
@@ -151,6 +165,7 @@ def gemm_nt(a, b, out=None, accumulate=False, out_dtype=None):
         out = torch.empty((M, N + (-N) % per16), dtype=odt, device=a.device)[:, :N]
     else:
         ab, ot, _ = _types(a, b, out.dtype)
+    _require_device(a, out=out)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must have shape (M, N)")
     _check(lib().gemm_nt_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
@@ -166,6 +181,7 @@ def gemm_nt_batched(a, b, out=None, accumulate=False, out_dtype=None):
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form batched A @ B.T")
     P, M, K = a.shape
     N = b.shape[1]
+    _require_device(a, a=a, b=b)
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs an existing out")
@@ -174,6 +190,7 @@ def gemm_nt_batched(a, b, out=None, accumulate=False, out_dtype=None):
         out = torch.empty((P, M, N + (-N) % per16), dtype=odt, device=a.device)[:, :, :N]
     else:
         ab, ot, _ = _types(a, b, out.dtype)
+    _require_device(a, out=out)
     if tuple(out.shape) != (P, M, N):
         raise ValueError("out must have shape (P, M, N)")
     _check(lib().gemm_nt_ex(
@@ -212,6 +229,7 @@ def matmul(a, b, out=None, accumulate=False, out_dtype=None):
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not form a @ b")
     M, K = a.shape
     N = b.shape[1]
+    _require_device(a, a=a, b=b)
     a_order, lda = _order(a, 1)
     b_order, ldb = _order(b, 0)
     if out is None:
@@ -222,6 +240,7 @@ def matmul(a, b, out=None, accumulate=False, out_dtype=None):
         out = torch.empty((M, N + (-N) % per16), dtype=odt, device=a.device)[:, :N]
     else:
         ab, ot, _ = _types(a, b, out.dtype)
+    _require_device(a, out=out)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must have shape (M, N)")
     _check(lib().gemm_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, _ld(out, M, N),
@@ -231,6 +250,7 @@ def matmul(a, b, out=None, accumulate=False, out_dtype=None):
 
 def frag_copy(src, dst, num, col_major, direction):
     """Fragment copy between two contiguous device buffers of num_tiles * 128 bytes each."""
+    _require_device(src, src=src, dst=dst)
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("src and dst must be contiguous")
     nbytes = src.numel() * src.element_size()

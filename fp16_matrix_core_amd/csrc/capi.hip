@@ -2,8 +2,9 @@
 //
 // Every argument is checked on the host before any HIP call; a failed check
 // returns a negative status and records a message for fp16mc_last_error().
-// The messages follow the matrix-load page's habit of saying why a copy does
-// not fit ("doesn't fit any num in {4,2,1}").  Launches go through
+// Each message names the argument and the rule it breaks, as the matrix-load
+// lowering reports why a copy does not fit ("copy -> ldstmatrix", "What it
+// accepts" and "Algorithm" step 3).  Launches go through
 // hipLaunchKernel, whose return code becomes FP16MC_EHIP on failure.
 
 #include <hip/hip_runtime.h>
@@ -134,7 +135,7 @@ int gemm_nt_f16f32(const void* A, const void* B, float* Out, int64_t M, int64_t 
 int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_major, int direction,
               void* stream) {
   if (num != 1 && num != 2 && num != 4)
-    return fail(FP16MC_EINVAL, "layout doesn't fit any num in {4,2,1} (num=%d)", num);
+    return fail(FP16MC_EINVAL, "num=%d: a matrix load moves 1, 2 or 4 tiles", num);
   if (num_tiles < 0) return fail(FP16MC_EINVAL, "negative num_tiles %lld", (long long)num_tiles);
   if (num_tiles % num)
     return fail(FP16MC_EINVAL, "num_tiles=%lld is not a multiple of num=%d", (long long)num_tiles, num);

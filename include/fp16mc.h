@@ -66,7 +66,10 @@ int gemm_nt_f16f32(const void* A, const void* B, float* Out,
                    int64_t lda, int64_t ldb, int64_t ldo, void* stream);
 
 /*
- * `batch` independent products in one launch: problem b uses
+ * `batch` independent products in one launch: the product of "Blackwell
+ * Tensor Cores" ("The Accumulator's Lifetime": one 128x64 output tile from a
+ * 128x64 A and a 64x64 B, K accumulated slice by slice) repeated over many
+ * independent operand sets.  Problem b uses
  * A + b*strideA, B + b*strideB, Out + b*strideO (strides in elements) with
  * the shapes and row strides above.  Same preconditions per problem, plus
  * batch >= 0, strides >= 0, strideA and strideB multiples of 8, strideO a
@@ -214,6 +217,10 @@ const char* gemm_ex_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int a_o
 /*
  * Message describing the last failed call on this thread ("" if none).  The
  * pointer stays valid until the next call of this library on the thread.
+ * It plays the part of the (ok, message) pair with which "copy ->
+ * ldstmatrix" ("What it accepts") reports why a copy does not fit the
+ * matrix load: a rejected call returns a negative status and this text
+ * names the argument and the rule it breaks.
  */
 const char* fp16mc_last_error(void);
 

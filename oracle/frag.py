@@ -113,7 +113,7 @@ def _slot_table(num, col_major):
 
 def _check_num(num):
     if num not in NUMS:
-        raise ValueError(f"layout doesn't fit any num in {{4,2,1}} (num={num})")
+        raise ValueError(f"num={num}: a matrix load moves 1, 2 or 4 tiles")
 
 
 def _groups(n_items, per_group, what):

@@ -2,9 +2,8 @@
 and two type combinations, against the CPU oracle through the C ABI.
 
 Each shape below is chosen so that the plan logic picks the named
-configuration (asserted); shapes are ragged in M, N and K.  The large ones
-are checked on sampled rows -- the first and last three rows and 26 random
-ones, every column -- plus all-finite and untouched padding.  Out is
+configuration (asserted); shapes are ragged in M, N and K.  Every element
+is checked, plus all-finite and untouched padding.  Out is
 followed by GUARD rows of NaN that must stay untouched: the last row tile of
 every shape reaches past M, and the kernels rely on the output buffer's
 range to drop those rows.
@@ -94,11 +93,7 @@ def test_plan(f, plan, a_order, b_order, ab, out_fmt, acc):
     assert torch.equal(out[:, N:].view(view), pad_before.view(view)), "padding of Out written"
     assert torch.equal(buf[M:].view(view), guard_before.view(view)), "rows past M written"
     assert bool(torch.isfinite(out[:, :N]).all())
-    if M <= 64:
-        rows = np.arange(M)
-    else:
-        rows = np.unique(np.concatenate([[0, 1, 2, M - 3, M - 2, M - 1], rng.choice(M, 26, replace=False)]))
-    got = out[torch.from_numpy(rows).cuda(), :N].float().double().cpu().numpy()
-    ref, bound = oracle.gemm_nt_ex(A[rows], B, None if C is None else C[rows], ab=ab)
+    got = out[:, :N].float().double().cpu().numpy()
+    ref, bound = oracle.gemm_nt_ex(A, B, C, ab=ab)
     ok, worst, n_bad = oracle.within_bound_out(got, ref, bound, out_fmt)
     assert ok, f"{plan} {a_order}{b_order} {ab}->{out_fmt}: {n_bad} bad (worst {worst:.3g})"

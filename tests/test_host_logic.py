@@ -180,7 +180,7 @@ def test_empty_problems_enqueue_nothing(L):
 
 
 @pytest.mark.parametrize("args,code,needle", [
-    ((FAKE, FAKE, 8, 3, 0, 0), -1, "doesn't fit any num"),
+    ((FAKE, FAKE, 8, 3, 0, 0), -1, "1, 2 or 4 tiles"),
     ((FAKE, FAKE, 6, 4, 0, 0), -1, "not a multiple of num=4"),
     ((FAKE, FAKE, -4, 4, 0, 0), -1, "negative"),
     ((FAKE, FAKE, 8, 2, 2, 0), -1, "col_major"),
@@ -227,3 +227,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(f, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="not built"):
         f.lib()
+
+
+def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
+    """Host tensors never reach the library: their addresses would be handed to the kernels."""
+    torch = pytest.importorskip("torch")
+    import fp16_matrix_core_amd as f
+
+    def no_call():
+        raise AssertionError("the library was reached with a host tensor")
+    monkeypatch.setattr(f, "lib", no_call)
+    a = torch.zeros((16, 16), dtype=torch.float16)
+    b = torch.zeros((8, 16), dtype=torch.float16)
+    out = torch.zeros((16, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f.gemm_nt(a, b, out)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f.gemm_nt(a, b)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f.gemm_nt_batched(a[None], b[None], out[None])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f.matmul(a, b.t(), out)
+    src = torch.zeros(64, dtype=torch.int16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f.frag_copy(src, torch.zeros_like(src), 1, False, f.FRAG_LOAD)

@@ -169,3 +169,20 @@ def test_rejects_bad_arguments():
         oracle.frag_load(np.zeros(64 * 2 + 8, np.uint16), 2, False)
     with pytest.raises(ValueError):
         oracle.frag_store(np.zeros(33, np.uint32), 1, False)
+
+
+@pytest.mark.parametrize("num", [1, 2, 4])
+@pytest.mark.parametrize("col_major", [False, True])
+def test_image_index_names_the_element_the_image_builders_place(num, col_major):
+    """image_index against images built by concatenation / transposition (no stride arithmetic):
+    every (r, c, t) lands on its own label, and the offsets cover one group image exactly once."""
+    tiles = _tiles_index_valued(1, num)
+    image = _image_col_major(tiles) if col_major else _image_row_major(tiles)
+    seen = []
+    for t in range(num):
+        for r in range(8):
+            for c in range(8):
+                off = oracle.image_index(num, col_major, r, c, t)
+                assert image[off] == tiles[0, t, r, c], (num, col_major, r, c, t, off)
+                seen.append(off)
+    assert sorted(seen) == list(range(64 * num))
