@@ -11,7 +11,7 @@ synchronisations; one JSON line on stdout.
 Besides the headline, the same line carries:
   roofline      the GEMM kernel against the dense fp16 MFMA peak, its
                 duration from HIP events recorded on the launch stream, and the
-                HBM traffic measured with rocprofv3 counters when the committed
+                L2-miss traffic measured with rocprofv3 counters when the committed
                 summary matches the current kernel source;
   cpu_baseline  the CPU oracle (numpy float64) on a bounded row sample of the
                 same workload, timed on this host;
@@ -47,8 +47,10 @@ PEAK_TFLOPS = 2516.6       # MI355X dense fp16 MFMA: 256 CU x 4096 flop/clk x 2.
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 GEMM_SOURCES = ["fp16_matrix_core_amd/csrc/gemm_kernels.hpp", "fp16_matrix_core_amd/csrc/gemm_nt.hip",
                 "fp16_matrix_core_amd/csrc/layout.hpp", "fp16_matrix_core_amd/csrc/kernels.hpp"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_8192_l2_miss_traffic.txt")
 CEILING_LIB = os.path.join(ROOT, "libbench_ceiling.so")
+PMC_GEMM_LAUNCHES = 30     # counter passes: launches of the 8192^3 product ...
+PMC_MFMA_LAUNCHES = 6      # ... and of the MFMA-only loop
 
 
 def log(*a):
@@ -70,7 +72,7 @@ def gemm_source_hash():
 
 
 def read_traffic(kernel_hash):
-    """HBM bytes per launch from the committed counter summary, if it matches this kernel source."""
+    """L2-miss bytes per launch from the committed counter summary, if it matches this kernel source."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     kv = {}
@@ -81,7 +83,7 @@ def read_traffic(kernel_hash):
     if kv.get("source_hash") != kernel_hash:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["l2_miss_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -355,14 +357,15 @@ def bench_ceilings(torch, stream, a, reps=10):
 
 
 def pmc_pass(torch, f):
-    """A short program for rocprofv3 counter passes: three 8192^3 launches, three
-    copies of 1 GiB (the counter calibration), two MFMA-only loops on the
-    workload's values, and one call of each frag_copy variant (2^20 tiles)."""
+    """A short program for rocprofv3 counter passes: PMC_GEMM_LAUNCHES 8192^3
+    launches, three copies of 1 GiB (the counter calibration), PMC_MFMA_LAUNCHES
+    MFMA-only loops on the workload's values, and one call of each frag_copy
+    variant (2^20 tiles)."""
     from fp16_matrix_core_amd import inputs
     A, B = inputs.large_square()
     a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
     out = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
-    for _ in range(3):
+    for _ in range(PMC_GEMM_LAUNCHES):      # the summaries use the later, clock-settled ones
         f.gemm_nt(a, b, out)
     torch.cuda.synchronize()
     src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -374,7 +377,7 @@ def pmc_pass(torch, f):
     sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
     sp = torch.cuda.current_stream().cuda_stream
     flat = a.reshape(-1)
-    for _ in range(2):
+    for _ in range(PMC_MFMA_LAUNCHES):
         if L.ceiling_mfma(flat.data_ptr(), flat.numel() * 2, sink.data_ptr(), 16, 4096, 256, sp) != 0:
             raise RuntimeError("ceiling_mfma failed")
     torch.cuda.synchronize()
@@ -387,7 +390,8 @@ def pmc_pass(torch, f):
             for direction in (0, 1, 2):
                 f.frag_copy_raw(img.data_ptr(), frag.data_ptr(), n_tiles, num, col, direction, sp)
     torch.cuda.synchronize()
-    log("pmc pass done: 3 x gemm_nt 8192^3, 3 x copy of 1 GiB, 2 x MFMA loop, 18 x frag_copy")
+    log(f"pmc pass done: {PMC_GEMM_LAUNCHES} x gemm_nt 8192^3, 3 x copy of 1 GiB, {PMC_MFMA_LAUNCHES} x MFMA loop, "
+        "18 x frag_copy")
 
 
 def run_secondary(torch, f, stream, a, b, A, B):
