@@ -540,9 +540,16 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int kk, Frags& f) FP16MC_INLINE {
     static_for<C::SI + C::SJ>([&](auto x) { read_one(as, bs, kk, f, x); });
   };
+  // Fresh 16-bit outputs of the four-wavefront 16x16x32 tiles leave through LDS
+  // (epilogue below).  Their MFMAs take B's fragment first, which transposes
+  // each 16x16 accumulator: lane l then holds row l%16 and the four
+  // consecutive columns 4(l/16) .. 4(l/16)+3, i.e. 8 bytes of one output row
+  // once rounded.  Each element is the same sum of the same products.
+  constexpr bool kLdsOut = sizeof(OutT) == 2 && !ACC && C::MI == 16 && C::NT == 256;
   auto mfma = [&](const Frags& f, int n) FP16MC_INLINE {
     const int si = n / C::SJ, sj = n % C::SJ;
-    acc[si][sj] = In::mma(f.a[si], f.b[sj], acc[si][sj]);
+    if constexpr (kLdsOut) acc[si][sj] = In::mma(f.b[sj], f.a[si], acc[si][sj]);
+    else acc[si][sj] = In::mma(f.a[si], f.b[sj], acc[si][sj]);
   };
   auto mfma_all = [&](const Frags& f) FP16MC_INLINE { static_for<NMF>([&](auto n) { mfma(f, decltype(n)::value); }); };
   // Wait until at most `n` direct loads of this thread are in flight and its
@@ -804,6 +811,76 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       read_frags(as, bs, kk, f0);
       mfma_all(f0);
     }
+  }
+
+  // ---- 16-bit epilogue through LDS (the store direction of the fragment
+  // copy: register fragments -> shared memory -> whole rows).  Wavefront w
+  // owns one K-loop stage array as its staging region (stage a0, a1, b0, b1
+  // for w = 0..3), free once every wavefront is past its last fragment read.
+  // Each lane rounds its four values per tile and writes them as 8 bytes at
+  // their place in a row-major (WTM x WTN) image of the wave tile (rows
+  // swizzled by OutSwizzle, so that the 16 lanes writing 16 different rows
+  // hit 16 different bank groups); the wavefront then reads the image back
+  // as 16-byte row pieces, one row of the wave tile per WTN/8 lanes, and
+  // stores them with 16-byte stores: every store instruction writes whole
+  // row pieces of WTN values, against 2-byte stores of one element per lane.
+  // A row piece that straddles N is stored element by element, so the ldo
+  // padding is never written; rows past M fall outside the output buffer's
+  // range.  (Accumulating 16-bit outputs keep the register epilogue below:
+  // adding the previous values read from the image in the accumulator's
+  // layout made the register allocator split the accumulators and spill.)
+  if constexpr (kLdsOut) {
+    using OS = OutSwizzle<2 * C::WTN>;
+    constexpr int kRowsPerAccess = 1024 / OS::kRowBytes;      // rows of the image per 1 KiB wavefront access
+    constexpr int kAccesses = C::WTM / kRowsPerAccess;        // 16-byte accesses per lane over the wave tile
+    static_assert(C::WM * C::WN == 4, "one staging region per wavefront: stages a0, a1, b0, b1");
+    static_assert(C::WTM * OS::kRowBytes <= C::A_STAGE && C::WTM * OS::kRowBytes <= C::B_STAGE,
+                  "a wave tile's 16-bit image fits one stage array");
+    static_assert(C::WTM % kRowsPerAccess == 0, "whole 1 KiB accesses");
+    unsigned char* region = wave == 0 ? lds_a0 : wave == 1 ? lds_a1 : wave == 2 ? lds_b0 : lds_b1;
+    const int row0 = wm * C::WTM, col0 = wn * C::WTN;           // wave tile inside the workgroup tile
+    const int ldo_b2 = static_cast<int>(ldo) * 2;               // bytes per row of Out
+    // LDS byte offset of a lane's four values of tile (si, sj) in the image
+    auto acc_off = [&](int si, int sj) {
+      const int r = si * 16 + (lane & 15);
+      const int col = sj * 16 + 4 * (lane >> 4);
+      return OS::offset_bytes(r, col >> 3) + 2 * (col & 7);
+    };
+    // every wavefront is past its last read of the stages
+    publish_keep(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int si = 0; si < C::SI; ++si)
+#pragma unroll
+      for (int sj = 0; sj < C::SJ; ++sj) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[si][sj][e];
+        unsigned int* w = reinterpret_cast<unsigned int*>(region + acc_off(si, sj));
+        unsigned int h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(unsigned short, static_cast<OutT>(v[e]));
+        w[0] = h[0] | (h[1] << 16);
+        w[1] = h[2] | (h[3] << 16);
+        sched_fence();   // one tile at a time: no hoisted reads holding registers
+      }
+#pragma unroll
+    for (int p = 0; p < kAccesses; ++p) {
+      const int r = p * kRowsPerAccess + lane / OS::kChunks;
+      const int c = lane % OS::kChunks;                       // logical chunk of row r
+      const u32x4 val = *reinterpret_cast<const u32x4*>(region + OS::offset_bytes(r, c));
+      const int col = col0 + 8 * c;                            // first column, inside the workgroup tile
+      const unsigned off = static_cast<unsigned>((row0 + r) * ldo_b2 + col * 2);
+      if (col + 8 <= o_cols) {
+        __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, off, 0, kAux);
+      } else if (col < o_cols) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < o_cols)
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(val[e >> 1] >> (16 * (e & 1))), orsrc,
+                                                  off + 2 * e, 0, kAux);
+      }
+    }
+    return;
   }
 
   // ---- epilogue: each row block's values in the (c, t, v) layout, plus the

@@ -130,6 +130,30 @@ struct TrSwizzle {
 };
 
 // ---------------------------------------------------------------------------
+// 16-bit output tiles staged in LDS.  Row r of a wave tile of 16-bit values
+// fills RowBytes (64, 128 or 256) bytes; its 16-byte chunk c sits at
+// physical chunk c ^ key(r) with key(r) = (r / (256 / RowBytes)) mod
+// (RowBytes / 16).  The accumulator writes put the 16 lanes of one 4-column
+// group on 16 consecutive rows at one logical chunk: the rows that share a
+// 256-byte bank window (256 / RowBytes of them) differ in their window
+// offset, the others in their key, so the 16 land on 16 different 16-byte
+// bank groups.  Reading back, the lanes of a row read its chunks in order:
+// each 1 KiB access covers contiguous rows.
+// ---------------------------------------------------------------------------
+template <int RowBytes>
+struct OutSwizzle {
+  static_assert(RowBytes == 64 || RowBytes == 128 || RowBytes == 256, "rows of 32, 64 or 128 16-bit values");
+  static constexpr int kRowBytes = RowBytes;
+  static constexpr int kChunks = RowBytes / 16;
+  FP16MC_HD static constexpr int key(int row) { return (row / (256 / RowBytes)) & (kChunks - 1); }
+  FP16MC_HD static constexpr int phys_chunk(int row, int chunk) { return chunk ^ key(row); }
+  FP16MC_HD static constexpr int logical_chunk(int row, int phys) { return phys ^ key(row); }
+  FP16MC_HD static constexpr int offset_bytes(int row, int chunk) {
+    return row * RowBytes + (phys_chunk(row, chunk) << 4);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // v_mfma_f32_32x32x16_f16: D(32x32) += X(32x16) * Y(16x32), fp16 in, fp32 acc.
 // Operands: lane l supplies 8 fp16 of X row (l % 32), and 8 fp16 of Y column
 // (l % 32), both at k = 8*(l / 32) + e, e in [0, 8).

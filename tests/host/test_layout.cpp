@@ -247,6 +247,45 @@ void check_tr_swizzle(int bk) {
   }
 }
 
+// 16-bit output staging: bijection per row; the accumulator writes (16
+// lanes of one 4-column group on 16 consecutive rows, 8 bytes each) land on 16
+// distinct 16-byte bank groups; the read-back accesses cover contiguous 1 KiB.
+template <int RowBytes>
+void check_out_swizzle() {
+  using Z = OutSwizzle<RowBytes>;
+  const int kc = Z::kChunks;
+  CHECK(kc * 16 == RowBytes, "out chunks per row");
+  for (int r = 0; r < 256; ++r) {
+    std::set<int> seen;
+    for (int c = 0; c < kc; ++c) {
+      seen.insert(Z::phys_chunk(r, c));
+      CHECK(Z::logical_chunk(r, Z::phys_chunk(r, c)) == c, "out inverse");
+    }
+    CHECK((int)seen.size() == kc, "out swizzle not a bijection (%d-byte rows, row %d)", RowBytes, r);
+  }
+  const int width = RowBytes / 2;                      // 16-bit values per row
+  for (int si = 0; si < 8; ++si)
+    for (int col4 = 0; col4 < width; col4 += 4) {      // a 4-column group: lanes 16 q .. 16 q + 15
+      std::set<int> groups;
+      for (int i = 0; i < 16; ++i) {
+        const int r = 16 * si + i;
+        const int off = Z::offset_bytes(r, col4 >> 3) + 2 * (col4 & 7);
+        groups.insert((off % 256) / 16);
+      }
+      CHECK((int)groups.size() == 16, "out staging write conflict (%d-byte rows, si %d, col %d)", RowBytes, si, col4);
+    }
+  const int rows_per_access = 1024 / RowBytes;
+  for (int p = 0; p < 8; ++p) {
+    std::set<int> offs;
+    for (int l = 0; l < 64; ++l) {
+      const int r = p * rows_per_access + l / kc;
+      offs.insert(Z::offset_bytes(r, l % kc));
+    }
+    CHECK((int)offs.size() == 64 && *offs.begin() == p * 1024 && *offs.rbegin() == p * 1024 + 63 * 16,
+          "out read-back access not a contiguous 1 KiB (%d-byte rows, access %d)", RowBytes, p);
+  }
+}
+
 int main() {
   check_swizzle<64>();
   check_swizzle<128>();
@@ -383,6 +422,9 @@ int main() {
     }
     CHECK(ms.size() == 4 && ns.size() == 8, "grouped_tile block shape");
   }
+  check_out_swizzle<64>();
+  check_out_swizzle<128>();
+  check_out_swizzle<256>();
   printf("OK %d\n", n_checks);
   return 0;
 }

@@ -37,7 +37,7 @@ PLAN_SHAPES = {
 }
 ORDERS = [("k", "k"), ("k", "mn"), ("mn", "k"), ("mn", "mn")]
 GUARD = 37
-TYPES = [("f16", "f32", False), ("bf16", "bf16", True)]
+TYPES = [("f16", "f32", False), ("bf16", "bf16", True), ("f16", "f16", False)]
 
 
 @pytest.fixture(scope="module")
