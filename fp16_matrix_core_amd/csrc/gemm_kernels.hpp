@@ -71,6 +71,15 @@ struct InF16 {
   static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+  // The same instruction with the accumulator tied to one AGPR quad, two
+  // wait states after whatever precedes it (a write of the accumulator's
+  // initial value needs them; between MFMAs the matrix pipe is the bound, so
+  // they cost nothing).  The result's read hazard is the caller's: see
+  // tied_mma_fence.
+  static __device__ __forceinline__ f32x4 mma_tied(V8 a, V8 b, f32x4 c) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
 };
 struct InBF16 {
   typedef bf16x8 V8;
@@ -79,6 +88,10 @@ struct InBF16 {
   }
   static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma_tied(V8 a, V8 b, f32x4 c) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
   }
 };
 
@@ -181,7 +194,7 @@ using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // per-fragment LDS offsets do not fit beside two 16x16 fragment sets) and
 // TT, which did not, was 13% slower.
 using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
-using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4>;
+using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
 // Tall 64x32 tiles for N <= 32: the product streams A (read by one
 // workgroup each, non-temporal) against a B that every workgroup shares.
 // 16384x8x16384: 93 us against 118 us for a dedicated register-streaming
@@ -546,10 +559,40 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // consecutive columns 4(l/16) .. 4(l/16)+3, i.e. 8 bytes of one output row
   // once rounded.  Each element is the same sum of the same products.
   constexpr bool kLdsOut = sizeof(OutT) == 2 && !ACC && C::MI == 16 && C::NT == 256;
+  // With an MN-contiguous operand the 16x16x32 kernels hold two more sets of
+  // per-fragment LDS offsets, and the register allocator, free to give an
+  // MFMA's result other registers than its accumulator input, then shuffled
+  // the 256 accumulators between AGPRs (some 400 moves per K-loop iteration,
+  // or spills).  Those kernels issue the MFMA as inline assembly with the
+  // accumulator tied to its AGPRs, which leaves the result-read hazard to
+  // tied_mma_fence below.
+  constexpr bool kTied = C::MI == 16 && (A_MN || B_MN);
   auto mfma = [&](const Frags& f, int n) FP16MC_INLINE {
     const int si = n / C::SJ, sj = n % C::SJ;
-    if constexpr (kLdsOut) acc[si][sj] = In::mma(f.b[sj], f.a[si], acc[si][sj]);
-    else acc[si][sj] = In::mma(f.a[si], f.b[sj], acc[si][sj]);
+    const auto& x = kLdsOut ? f.b[sj] : f.a[si];
+    const auto& y = kLdsOut ? f.a[si] : f.b[sj];
+    if constexpr (kTied) acc[si][sj] = In::mma_tied(x, y, acc[si][sj]);
+    else acc[si][sj] = In::mma(x, y, acc[si][sj]);
+  };
+  // The compiler inserts no wait states around an MFMA written as inline
+  // assembly.  Before each one (inside the statement, mma_tied): the zeroes
+  // the compiler writes into the accumulators must have landed before an
+  // MFMA reads them as its C operand (without the wait, elements of the
+  // accumulators that the first MFMAs read came out wrong, varying from run
+  // to run).  After the last one (tied_mma_fence): before anything
+  // other than the next MFMA reads an accumulator, wait longer than the
+  // instruction's result latency (32 wait states, against at most 19 in the
+  // CDNA3 ISA's dependency table), then pass every accumulator through an
+  // empty statement ordered after the wait, so that no read of them can be
+  // scheduled above it.
+  auto tied_mma_fence = [&]() FP16MC_INLINE {
+    if constexpr (kTied) {
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+      for (int si = 0; si < C::SI; ++si)
+#pragma unroll
+        for (int sj = 0; sj < C::SJ; ++sj) asm volatile("" : "+a"(acc[si][sj]));
+    }
   };
   auto mfma_all = [&](const Frags& f) FP16MC_INLINE { static_for<NMF>([&](auto n) { mfma(f, decltype(n)::value); }); };
   // Wait until at most `n` direct loads of this thread are in flight and its
@@ -829,6 +872,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // range.  (Accumulating 16-bit outputs keep the register epilogue below:
   // adding the previous values read from the image in the accumulator's
   // layout made the register allocator split the accumulators and spill.)
+  tied_mma_fence();
   if constexpr (kLdsOut) {
     using OS = OutSwizzle<2 * C::WTN>;
     constexpr int kRowsPerAccess = 1024 / OS::kRowBytes;      // rows of the image per 1 KiB wavefront access

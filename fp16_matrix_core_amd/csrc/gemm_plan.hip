@@ -77,7 +77,7 @@ const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn) {
   switch (plan) {
     case GemmPlan::kWave32: return "wave32x32_mfma32x32x16";
     case GemmPlan::kWg128x64: return mn ? "wg128x64_w4_mfma32x32x16" : "wg128x64_w4_mfma16x16x32";
-    case GemmPlan::kWg256: return mn ? "wg256x256_w4_mfma32x32x16" : "wg256x256_w4_mfma16x16x32";
+    case GemmPlan::kWg256: return "wg256x256_w4_mfma16x16x32";
     case GemmPlan::kTall: return "tall64x32_w2_mfma32x32x16";
     case GemmPlan::kWg128x64Stream: return "wg128x64s_w4_mfma32x32x16";
     case GemmPlan::kWg256x128: return mn ? "wg256x128_w4_mfma32x32x16" : "wg256x128_w4_mfma16x16x32";
