@@ -310,7 +310,7 @@ def ceiling_lib():
     L.ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_void_p]
     L.ceiling_mfma.restype = ctypes.c_int
-    L.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     L.ceiling_copy.restype = ctypes.c_int
     return L
 
@@ -342,17 +342,21 @@ def bench_ceilings(torch, stream, a, reps=10):
     nbytes = 1 << 27                    # 128 MiB read + 128 MiB written per call
     bufs = [(torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0),
              torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")) for _ in range(3)]
-    i = [0]
+    shapes = {}
+    for shape, label in ((0, "1x512"), (1, "2x256"), (2, "4x256"), (3, "1x256")):
+        i = [0]
 
-    def copy():
-        s_, d_ = bufs[i[0] % 3]
-        i[0] += 1
-        if L.ceiling_copy(s_.data_ptr(), d_.data_ptr(), nbytes, sp) != 0:
-            raise RuntimeError("ceiling_copy failed")
-    for _ in range(5):
-        copy()
-    ms = timer.time(copy, 20)
-    res["copy_2^28B_GB/s"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+        def copy():
+            s_, d_ = bufs[i[0] % 3]
+            i[0] += 1
+            if L.ceiling_copy(s_.data_ptr(), d_.data_ptr(), nbytes, shape, sp) != 0:
+                raise RuntimeError("ceiling_copy failed")
+        for _ in range(5):
+            copy()
+        ms = timer.time(copy, 20)
+        shapes[label] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    res["copy_shapes_GB/s"] = shapes
+    res["copy_2^28B_GB/s"] = max(shapes.values())
     return res
 
 
@@ -396,13 +400,22 @@ def pmc_pass(torch, f):
 
 def run_secondary(torch, f, stream, a, b, A, B):
     log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders")
-    return {"ceilings": bench_ceilings(torch, stream, a),
-            "frag_copy": bench_frag(torch, f, stream),
-            "batched_4096x128x64x64": bench_batched(torch, f, stream),
-            "skinny_16384x8x16384": bench_skinny(torch, f, stream),
-            "small": bench_small(torch, f, stream),
-            "gemm_8192_types": bench_types(torch, f, stream, a, b),
-            "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
+    sec = {"ceilings": bench_ceilings(torch, stream, a),
+           "frag_copy": bench_frag(torch, f, stream),
+           "batched_4096x128x64x64": bench_batched(torch, f, stream),
+           "skinny_16384x8x16384": bench_skinny(torch, f, stream),
+           "small": bench_small(torch, f, stream),
+           "gemm_8192_types": bench_types(torch, f, stream, a, b),
+           "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
+    # the bandwidth-bound kernels against what a plain copy moves on this machine
+    copy = sec["ceilings"]["copy_2^28B_GB/s"]
+    fc = sec["frag_copy"]
+    fc["copy_ceiling_GB/s"] = copy
+    fc["min_frac_of_copy"] = round(min(fc["results"].values()) / copy, 4)
+    fc["max_frac_of_copy"] = round(max(fc["results"].values()) / copy, 4)
+    for key in ("batched_4096x128x64x64", "skinny_16384x8x16384"):
+        sec[key]["frac_of_copy"] = round(sec[key]["GB/s"] / copy, 4)
+    return sec
 
 
 def main():

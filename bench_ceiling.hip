@@ -10,9 +10,10 @@
 //                 product's own operand values it shows how far the operand
 //                 data alone pulls the clock down (the chip is power-limited
 //                 with random operands); fed with zeros, the issue-rate peak.
-//   ceiling_copy  a plain 16-byte copy with non-temporal loads and stores:
-//                 what the memory system gives a pure streaming kernel of
-//                 the same size as a fragment copy.
+//   ceiling_copy  a plain 16-byte copy with non-temporal loads and stores,
+//                 in four access shapes: what the memory system gives a
+//                 pure streaming kernel of the same size as a fragment copy
+//                 (the best shape differs from box to box by a few percent).
 //
 // One workgroup of four wavefronts per CU for the MFMA loop (a 256-register
 // accumulator leaves room for one wavefront per SIMD).
@@ -82,16 +83,16 @@ __global__ void __launch_bounds__(256, 1) mfma_loop(const f16x8* __restrict__ op
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// Each thread copies 4 chunks of 16 bytes, 256 chunks apart (whole 4 KiB per
-// workgroup and step); n16 is a multiple of 1024.
-__global__ void __launch_bounds__(256) copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                              int64_t n16) {
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
-  u32x4 v[4];
+// Each thread copies D chunks of 16 bytes, T chunks apart (T threads per
+// workgroup, T*D chunks per workgroup); n16 is a multiple of 4096.
+template <int D, int T>
+__global__ void __launch_bounds__(T) copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * T * D + threadIdx.x;
+  u32x4 v[D];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(src + base + 256 * k);
+  for (int k = 0; k < D; ++k) v[k] = __builtin_nontemporal_load(src + base + T * k);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v[k], dst + base + 256 * k);
+  for (int k = 0; k < D; ++k) __builtin_nontemporal_store(v[k], dst + base + T * k);
 }
 
 }  // namespace
@@ -112,12 +113,21 @@ int ceiling_mfma(const void* ops, int64_t ops_bytes, float* sink, int mi, int it
   return static_cast<int>(hipGetLastError());
 }
 
-// Copies `bytes` (a multiple of 16 KiB) from src to dst, both 16-byte aligned.
-int ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream) {
-  if (bytes <= 0 || bytes % 16384 != 0) return -1;
+// Copies `bytes` (a multiple of 64 KiB) from src to dst, both 16-byte aligned,
+// with one of four access shapes (chunks per thread x threads per workgroup:
+// 0: 1 x 512, 1: 2 x 256, 2: 4 x 256, 3: 1 x 256); -1 for bad arguments.
+int ceiling_copy(const void* src, void* dst, int64_t bytes, int shape, void* stream) {
+  if (bytes <= 0 || bytes % 65536 != 0 || shape < 0 || shape > 3) return -1;
   const int64_t n16 = bytes / 16;
-  hipLaunchKernelGGL(copy16, dim3(static_cast<unsigned>(n16 / 1024)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (shape) {
+    case 0: hipLaunchKernelGGL((copy16<1, 512>), dim3(static_cast<unsigned>(n16 / 512)), dim3(512), 0, st, s, d, n16); break;
+    case 1: hipLaunchKernelGGL((copy16<2, 256>), dim3(static_cast<unsigned>(n16 / 512)), dim3(256), 0, st, s, d, n16); break;
+    case 2: hipLaunchKernelGGL((copy16<4, 256>), dim3(static_cast<unsigned>(n16 / 1024)), dim3(256), 0, st, s, d, n16); break;
+    default: hipLaunchKernelGGL((copy16<1, 256>), dim3(static_cast<unsigned>(n16 / 256)), dim3(256), 0, st, s, d, n16); break;
+  }
   return static_cast<int>(hipGetLastError());
 }
 
