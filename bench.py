@@ -312,6 +312,9 @@ def ceiling_lib():
     L.ceiling_mfma.restype = ctypes.c_int
     L.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     L.ceiling_copy.restype = ctypes.c_int
+    L.ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.ceiling_stream.restype = ctypes.c_int
     return L
 
 
@@ -357,6 +360,22 @@ def bench_ceilings(torch, stream, a, reps=10):
         shapes[label] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
     res["copy_shapes_GB/s"] = shapes
     res["copy_2^28B_GB/s"] = max(shapes.values())
+    del bufs
+    # the batched product's stream: per problem 24 KiB read (A 128x64, B 64x64 fp16), 32 KiB written
+    units, rd, wr = 4096, 24576, 32768
+    sets = [(torch.empty(units * rd // 4, dtype=torch.float32, device="cuda").fill_(1.0),
+             torch.empty(units * wr // 4, dtype=torch.float32, device="cuda")) for _ in range(3)]
+    i = [0]
+
+    def stream():
+        s_, d_ = sets[i[0] % 3]
+        i[0] += 1
+        if L.ceiling_stream(s_.data_ptr(), d_.data_ptr(), units, rd, wr, sp) != 0:
+            raise RuntimeError("ceiling_stream failed")
+    for _ in range(5):
+        stream()
+    ms = timer.time(stream, 20)
+    res["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
     return res
 
 
@@ -415,6 +434,8 @@ def run_secondary(torch, f, stream, a, b, A, B):
     fc["max_frac_of_copy"] = round(max(fc["results"].values()) / copy, 4)
     for key in ("batched_4096x128x64x64", "skinny_16384x8x16384"):
         sec[key]["frac_of_copy"] = round(sec[key]["GB/s"] / copy, 4)
+    mix = sec["ceilings"]["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"]
+    sec["batched_4096x128x64x64"]["frac_of_same_mix_stream"] = round(sec["batched_4096x128x64x64"]["GB/s"] / mix, 4)
     return sec
 
 

@@ -14,6 +14,8 @@
 //                 in four access shapes: what the memory system gives a
 //                 pure streaming kernel of the same size as a fragment copy
 //                 (the best shape differs from box to box by a few percent).
+//   ceiling_stream  a read/write stream with the batched product's mix per
+//                 workgroup (its operands read, its output written once).
 //
 // One workgroup of four wavefronts per CU for the MFMA loop (a 256-register
 // accumulator leaves room for one wavefront per SIMD).
@@ -95,6 +97,20 @@ __global__ void __launch_bounds__(T) copy16(const u32x4* __restrict__ src, u32x4
   for (int k = 0; k < D; ++k) __builtin_nontemporal_store(v[k], dst + base + T * k);
 }
 
+// One workgroup per unit: reads rd16 16-byte chunks of its source span and
+// writes wr16 chunks of its destination span (both non-temporal), the
+// written values derived from the read ones so that no load is dropped.
+// The same read/write mix per workgroup as a batched product whose
+// problems each read A and B and write their output once.
+__global__ void __launch_bounds__(256) stream_mix(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                  int rd16, int wr16) {
+  const u32x4* s = src + static_cast<int64_t>(blockIdx.x) * rd16;
+  u32x4* d = dst + static_cast<int64_t>(blockIdx.x) * wr16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < rd16; i += 256) acc ^= __builtin_nontemporal_load(s + i);
+  for (int i = threadIdx.x; i < wr16; i += 256) __builtin_nontemporal_store(acc + static_cast<unsigned>(i), d + i);
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +144,15 @@ int ceiling_copy(const void* src, void* dst, int64_t bytes, int shape, void* str
     case 2: hipLaunchKernelGGL((copy16<4, 256>), dim3(static_cast<unsigned>(n16 / 1024)), dim3(256), 0, st, s, d, n16); break;
     default: hipLaunchKernelGGL((copy16<1, 256>), dim3(static_cast<unsigned>(n16 / 256)), dim3(256), 0, st, s, d, n16); break;
   }
+  return static_cast<int>(hipGetLastError());
+}
+
+// `units` workgroups, each reading rd_bytes from src + u*rd_bytes and writing
+// wr_bytes to dst + u*wr_bytes (both multiples of 16); -1 for bad arguments.
+int ceiling_stream(const void* src, void* dst, int units, int rd_bytes, int wr_bytes, void* stream) {
+  if (units <= 0 || rd_bytes <= 0 || wr_bytes <= 0 || rd_bytes % 16 != 0 || wr_bytes % 16 != 0) return -1;
+  hipLaunchKernelGGL(stream_mix, dim3(units), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), rd_bytes / 16, wr_bytes / 16);
   return static_cast<int>(hipGetLastError());
 }
 

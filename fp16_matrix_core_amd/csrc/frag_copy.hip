@@ -12,13 +12,13 @@
 // One 64-lane wavefront carries two 32-lane fragments (lanes [0,32) and
 // [32,64)), i.e. two consecutive groups.
 //
-// Each workgroup walks blocks of 8 KiB of groups.  Both sides of a block
-// are contiguous 8 KiB spans in HBM: the image, and the fragments stored
-// lane-major (group, lane, num words).  The kernel is HBM-bound: 128 bytes
-// read and 128 bytes written per tile.  Every HBM access is
-// non-temporal (each byte is touched once; measured +8-11% over cached
-// accesses), and up to 16384 workgroups cover the 2^20-tile workload's 16384
-// blocks in one pass.
+// Each wavefront walks blocks of 1 KiB of groups on its own (no workgroup
+// barrier).  Both sides of a block are contiguous 1 KiB spans in HBM: the
+// image, and the fragments stored lane-major (group, lane, num words).  The
+// kernel is HBM-bound: 128 bytes read and 128 bytes written per tile.  Every
+// HBM access is non-temporal (each byte is touched once; measured +8-11%
+// over cached accesses), and up to 16384 workgroups of eight wavefronts
+// cover the 2^20-tile workload's 131072 blocks in one pass.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,10 +53,11 @@ struct Words<4> {
   static __device__ __forceinline__ void set(T& v, int t, unsigned int w) { v[t] = w; }
 };
 
-constexpr int kThreads = 256;
-constexpr int kBlockBytes = 8 * 1024;
-constexpr int kBlockChunks = kBlockBytes / 16;
-constexpr int kHalfWaves = kThreads / 32;
+constexpr int kThreads = 512;                 // eight wavefronts per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaveBytes = 1024;              // image (and fragment) bytes a wavefront moves per step
+constexpr int kWaveChunks = kWaveBytes / 16;  // one 16-byte chunk per lane
+constexpr int kMaxGrid = 16384;
 
 // Word t of the fragment of lane `l32` (0..31), read from a group image in LDS.
 template <int NUM, bool COL>
@@ -84,93 +85,89 @@ __device__ __forceinline__ void lds_write_word(unsigned short* img, int l32, int
   }
 }
 
+// The wavefront's LDS writes become visible to its own later reads: LDS
+// executes a wavefront's instructions in order; the wait and the compiler
+// barrier keep the reads of other lanes' words behind the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters untouched
+  asm volatile("" ::: "memory");
+}
+
 // DIR: 0 load (image -> fragment), 1 store (fragment -> image), 2 roundtrip.
-// The image side of a block always moves between HBM and LDS with 16-byte
-// accesses.  Its fragment side (group g holds 32 lanes of NUM words) is as
-// contiguous: the load direction stages it in LDS as well and writes it with
-// 16-byte stores (num = 1 and 2 would otherwise store 4 or 8 bytes per
-// lane; measured +1-2%), while the store direction reads it straight into
-// the lanes' registers, every fragment of the block in flight at once
-// (staging it measured 1-3% slower there).
+// Every wavefront works alone on its own 1 KiB spans: wave block w holds
+// groups [w * 8/NUM, (w+1) * 8/NUM) -- 1 KiB of image and 1 KiB of fragments
+// (lane-major, group after group), both contiguous in HBM.  Each lane moves
+// one 16-byte chunk of the source span into the wavefront's LDS region, the
+// two half-waves rebuild their groups' other side in a second region (the
+// words each lane owns: ds_read/ds_write of 4-byte words for row-major
+// images, b16 pairs for column-major ones), and each lane stores one 16-byte
+// chunk of the result.  No workgroup barrier: every wavefront streams as a
+// plain copy would (the access shape of the fastest plain copy measured on
+// gfx950: one 16-byte chunk per lane, 512-thread workgroups, every access
+// non-temporal), instead of each workgroup waiting for all of its 8 KiB to
+// arrive before any of it leaves.
 template <int NUM, bool COL, int DIR>
 __global__ void __launch_bounds__(kThreads)
-frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t groups, int64_t nblocks) {
+frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t groups, int64_t nwblocks) {
   constexpr int kGroupBytes = 128 * NUM;
-  constexpr int kGroupsPerBlock = kBlockBytes / kGroupBytes;
+  constexpr int kGroupsPerWave = kWaveBytes / kGroupBytes;
   constexpr int kGroupHalves = 64 * NUM;
   typedef typename Words<NUM>::T W;
 
-  __shared__ __attribute__((aligned(16))) u32x4 lds_a[kBlockChunks];                  // image
-  __shared__ __attribute__((aligned(16))) u32x4 lds_b[DIR == 1 ? 1 : kBlockChunks];   // fragments / 2nd image
+  __shared__ __attribute__((aligned(16))) u32x4 lds[kWaves][2][kWaveChunks];   // per wavefront: source, result
 
-  const int tid = threadIdx.x;
-  const int l32 = tid & 31;
-  const int hw = tid >> 5;  // half-wave: one 32-lane fragment at a time
-  unsigned short* img = reinterpret_cast<unsigned short*>(lds_a);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hw = lane >> 5;  // half-wave: one 32-lane fragment at a time
+  u32x4* in = lds[wave][0];
+  u32x4* out = lds[wave][1];
+  unsigned short* in_img = reinterpret_cast<unsigned short*>(in);
+  unsigned short* out_img = reinterpret_cast<unsigned short*>(out);
 
-  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-    const int64_t g0 = blk * kGroupsPerBlock;
-    const int ng = static_cast<int>((groups - g0) < kGroupsPerBlock ? (groups - g0) : kGroupsPerBlock);
+  for (int64_t wb = static_cast<int64_t>(blockIdx.x) * kWaves + wave; wb < nwblocks;
+       wb += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const int64_t g0 = wb * kGroupsPerWave;
+    const int ng = static_cast<int>((groups - g0) < kGroupsPerWave ? (groups - g0) : kGroupsPerWave);
     const int nchunks = ng * (kGroupBytes / 16);
+    const u32x4* s = static_cast<const u32x4*>(src) + g0 * (kGroupBytes / 16);
     u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
-
-    if constexpr (DIR == 0 || DIR == 2) {
-      // image: HBM -> LDS
-      const u32x4* s = static_cast<const u32x4*>(src) + g0 * (kGroupBytes / 16);
-      for (int c = tid; c < nchunks; c += kThreads) lds_a[c] = __builtin_nontemporal_load(s + c);
-      __syncthreads();
-      // image -> registers -> fragments (lane-major) or the second image, in LDS
-      for (int lg = hw; lg < ng; lg += kHalfWaves) {
+    if (lane < nchunks) in[lane] = __builtin_nontemporal_load(s + lane);
+    wave_lds_sync();
+    for (int lg = hw; lg < ng; lg += 2) {
+      if constexpr (DIR == 0) {
+        // image -> the lane's fragment words, lane-major
         W v;
 #pragma unroll
-        for (int t = 0; t < NUM; ++t) Words<NUM>::set(v, t, lds_read_word<NUM, COL>(img + lg * kGroupHalves, l32, t));
-        if constexpr (DIR == 0) {
-          reinterpret_cast<W*>(lds_b)[lg * 32 + l32] = v;
-        } else {
-          unsigned short* out = reinterpret_cast<unsigned short*>(lds_b) + lg * kGroupHalves;
+        for (int t = 0; t < NUM; ++t) Words<NUM>::set(v, t, lds_read_word<NUM, COL>(in_img + lg * kGroupHalves, l32, t));
+        reinterpret_cast<W*>(out)[lg * 32 + l32] = v;
+      } else if constexpr (DIR == 1) {
+        // the lane's fragment words -> their places in the image
+        const W v = reinterpret_cast<const W*>(in)[lg * 32 + l32];
 #pragma unroll
-          for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out, l32, t, Words<NUM>::get(v, t));
-        }
-      }
-      __syncthreads();
-      for (int c = tid; c < nchunks; c += kThreads) __builtin_nontemporal_store(lds_b[c], d + c);
-      __syncthreads();
-    } else {
-      // fragment: HBM -> VGPR -> LDS image.  In a full block every half-wave
-      // loads all its fragments before writing any, so that its loads (num
-      // words per lane each) are in flight together.
-      const W* frag = static_cast<const W*>(src) + g0 * 32 + l32;
-      if (ng == kGroupsPerBlock) {
-        constexpr int kIt = kGroupsPerBlock / kHalfWaves;
-        W v[kIt];
-#pragma unroll
-        for (int i = 0; i < kIt; ++i) v[i] = __builtin_nontemporal_load(frag + (hw + i * kHalfWaves) * 32);
-#pragma unroll
-        for (int i = 0; i < kIt; ++i)
-#pragma unroll
-          for (int t = 0; t < NUM; ++t)
-            lds_write_word<NUM, COL>(img + (hw + i * kHalfWaves) * kGroupHalves, l32, t, Words<NUM>::get(v[i], t));
+        for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out_img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
       } else {
-        for (int lg = hw; lg < ng; lg += kHalfWaves) {
-          const W v = __builtin_nontemporal_load(frag + lg * 32);
+        // image -> fragment words (registers) -> a second image
+        W v;
 #pragma unroll
-          for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
-        }
+        for (int t = 0; t < NUM; ++t) Words<NUM>::set(v, t, lds_read_word<NUM, COL>(in_img + lg * kGroupHalves, l32, t));
+#pragma unroll
+        for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out_img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
       }
-      __syncthreads();
-      // image: LDS -> HBM
-      for (int c = tid; c < nchunks; c += kThreads) __builtin_nontemporal_store(lds_a[c], d + c);
-      __syncthreads();
     }
+    wave_lds_sync();
+    if (lane < nchunks) __builtin_nontemporal_store(out[lane], d + lane);
+    wave_lds_sync();   // this step's reads of both regions precede the next step's writes
   }
 }
 
 template <int NUM, bool COL, int DIR>
 hipError_t launch_one(const void* src, void* dst, int64_t groups, hipStream_t stream) {
-  constexpr int kGroupsPerBlock = kBlockBytes / (128 * NUM);
-  int64_t nblocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  const int64_t grid = nblocks < 16384 ? nblocks : 16384;
-  void* args[] = {const_cast<void**>(&src), &dst, &groups, &nblocks};
+  constexpr int kGroupsPerWave = kWaveBytes / (128 * NUM);
+  int64_t nwblocks = (groups + kGroupsPerWave - 1) / kGroupsPerWave;
+  const int64_t blocks = (nwblocks + kWaves - 1) / kWaves;
+  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  void* args[] = {const_cast<void**>(&src), &dst, &groups, &nwblocks};
   return hipLaunchKernel(reinterpret_cast<const void*>(&frag_copy_kernel<NUM, COL, DIR>),
                          dim3(static_cast<unsigned>(grid)), dim3(kThreads), args, 0, stream);
 }
