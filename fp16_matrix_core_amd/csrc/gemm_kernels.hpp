@@ -175,8 +175,8 @@ using CfgWg64 = Cfg<64, 64, 2, 2, 8, 4, 1, 64, 0, 16>;
 using CfgWg64Mn = Cfg<64, 64, 2, 2, 8, 4, 1, 64>;
 // 128x64 tiles: 64-wide slices in three 24 KiB stages (two workgroups per CU
 // by LDS); measured 28% faster at 2048^3 than 32-wide slices in four stages.
-// As for every large-tile configuration below, K-contiguous operands use
-// 16x16x32 instructions and MN-contiguous ones 32x32x16 (the "Mn" twin).
+// K-contiguous operands use 16x16x32 instructions, MN-contiguous ones
+// 32x32x16 (the "Mn" twin; the larger tiles below use 16x16x32 for both).
 using CfgWg128x64 = Cfg<128, 64, 4, 1, 8, 3, 1, 64, 0, 16>;
 using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // 256x256 tiles: 64-wide slices in two 64 KiB stages (three do not fit in
@@ -190,11 +190,12 @@ using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // (it moves half the accumulator per flop); 8192^3 is 5-8% faster with it.
 // With the fragment reads interleaved the smaller tiles gain from it too
 // (256x128 and 128x128 5-10%, 128x64 2-3%; only single-slice K = 64 loses,
-// 7%). Operands stored MN-contiguous keep 32x32x16: NN and TN spilled (their
-// per-fragment LDS offsets do not fit beside two 16x16 fragment sets) and
-// TT, which did not, was 13% slower.
+// 7%). With an operand stored MN-contiguous the compiler's MFMA builtin made
+// NN and TN spill and TT run 13% slower (accumulators shuffled between
+// AGPRs); those kernels issue the MFMA with tied accumulators instead (see
+// kTied in the kernel): 8192^3 NN 842 -> 789 us, TT 839 -> 791 us, TN 842
+// -> 800 us against 32x32x16.
 using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
-using CfgWg256Mn = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
 // Tall 64x32 tiles for N <= 32: the product streams A (read by one
 // workgroup each, non-temporal) against a B that every workgroup shares.
 // 16384x8x16384: 93 us against 118 us for a dedicated register-streaming
@@ -209,10 +210,14 @@ using CfgWg128x64Stream = Cfg<128, 64, 4, 1, 8, 2, 2, 64, 7>;
 // Intermediate tiles for problems too small to fill the 256 CUs with
 // 256x256 tiles: 256x128 (three 48 KiB stages) and 128x128 (two 32 KiB
 // stages, two workgroups per CU).
+// With an MN-contiguous operand these two and the 256x256 tiles keep their
+// 16x16x32 configuration (accumulators tied to their AGPRs, see the
+// kernel): against 32x32x16, 8192x1024x8192 NN 117.7 -> 113.1 us, TN 118.9
+// -> 117.4 us, 6144^2x2048 NN 158.2 -> 153.7 us, TN 157.9 -> 152.5 us.  The
+// 128x64 and 64x64 tiles keep 32x32x16 for them (16x16x32 measured 1-2%
+// slower there: 2048^3 TN 26.2 -> 26.8 us, 1024^2x4096 17.2 -> 17.5 us).
 using CfgWg256x128 = Cfg<256, 128, 2, 2, 4, 3, 1, 64, 0, 16>;
-using CfgWg256x128Mn = Cfg<256, 128, 2, 2, 4, 3, 1, 64>;
 using CfgWg128x128 = Cfg<128, 128, 2, 2, 8, 2, 2, 64, 0, 16>;
-using CfgWg128x128Mn = Cfg<128, 128, 2, 2, 8, 2, 2, 64>;
 // Wide 32x64 tiles for M <= 32: the mirror of the tall tiles, B streamed.
 using CfgWide = Cfg<32, 64, 1, 2, 1, 4, 1, 64, 2>;
 
@@ -1060,11 +1065,11 @@ hipError_t launch_layout(GemmPlan plan, const GemmProblem& p, hipStream_t stream
   switch (plan) {
     case GemmPlan::kWave32: return launch_cfg<CfgWave32, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64: return launch_by_order<CfgWg128x64, CfgWg128x64Mn, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg256: return launch_by_order<CfgWg256, CfgWg256Mn, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256: return launch_cfg<CfgWg256, A_MN, B_MN>(p, stream);
     case GemmPlan::kTall: return launch_cfg<CfgTall, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg128x64Stream: return launch_cfg<CfgWg128x64Stream, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg256x128: return launch_by_order<CfgWg256x128, CfgWg256x128Mn, A_MN, B_MN>(p, stream);
-    case GemmPlan::kWg128x128: return launch_by_order<CfgWg128x128, CfgWg128x128Mn, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg256x128: return launch_cfg<CfgWg256x128, A_MN, B_MN>(p, stream);
+    case GemmPlan::kWg128x128: return launch_cfg<CfgWg128x128, A_MN, B_MN>(p, stream);
     case GemmPlan::kWide: return launch_cfg<CfgWide, A_MN, B_MN>(p, stream);
     case GemmPlan::kWg64: return launch_by_order<CfgWg64, CfgWg64Mn, A_MN, B_MN>(p, stream);
     default: return hipSuccess;

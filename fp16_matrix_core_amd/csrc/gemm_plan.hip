@@ -80,8 +80,8 @@ const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn) {
     case GemmPlan::kWg256: return "wg256x256_w4_mfma16x16x32";
     case GemmPlan::kTall: return "tall64x32_w2_mfma32x32x16";
     case GemmPlan::kWg128x64Stream: return "wg128x64s_w4_mfma32x32x16";
-    case GemmPlan::kWg256x128: return mn ? "wg256x128_w4_mfma32x32x16" : "wg256x128_w4_mfma16x16x32";
-    case GemmPlan::kWg128x128: return mn ? "wg128x128_w4_mfma32x32x16" : "wg128x128_w4_mfma16x16x32";
+    case GemmPlan::kWg256x128: return "wg256x128_w4_mfma16x16x32";
+    case GemmPlan::kWg128x128: return "wg128x128_w4_mfma16x16x32";
     case GemmPlan::kWide: return "wide32x64_w2_mfma32x32x16";
     case GemmPlan::kWg64: return mn ? "wg64x64_w4_mfma32x32x16" : "wg64x64_w4_mfma16x16x32";
     default: return nullptr;

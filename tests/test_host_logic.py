@@ -155,13 +155,14 @@ def test_plans_by_storage_order(L):
         assert f.plan_ex(16, 8, 16, 1, *order).startswith("wave32x32")
         assert f.plan_ex(8192, 8192, 8192, 1, *order).startswith("wg256x256")
     # large tiles use 16x16x32 instructions for K-contiguous operands; with an
-    # MN-contiguous operand the 256x256 tiles do too, the smaller ones 32x32x16
+    # MN-contiguous operand the 256x256, 256x128 and 128x128 tiles do too, the
+    # 128x64 ones 32x32x16
     for shape, name in (((8192, 8192, 8192), "wg256x256_w4"), ((8192, 1024, 8192), "wg256x128_w4"),
                         ((6144, 6144, 2048), "wg128x128_w4"), ((2048, 2048, 2048), "wg128x64_w4")):
         assert f.plan_ex(*shape, 1, 0, 0) == name + "_mfma16x16x32"
         assert f.plan(*shape) == name + "_mfma16x16x32"
         for order in ((1, 0), (0, 1), (1, 1)):
-            mn_mfma = "_mfma16x16x32" if name == "wg256x256_w4" else "_mfma32x32x16"
+            mn_mfma = "_mfma32x32x16" if name == "wg128x64_w4" else "_mfma16x16x32"
             assert f.plan_ex(*shape, 1, *order) == name + mn_mfma
     assert f.plan(128, 64, 64, 4096) == "wg128x64s_w4_mfma32x32x16"
     assert f.plan(16384, 8, 16384) == "tall64x32_w2_mfma32x32x16"
