@@ -33,7 +33,7 @@ PLAN_SHAPES = {
     "wg128x64": (300, 520, 200),
     "wg128x128": (4100, 2050, 100),
     "wg256x128": (1003, 4105, 8200),
-    "wg256x256": (8100, 2000, 4100),
+    "wg256x256": (8100, 2003, 4100),      # N % 8 = 3: 16-bit row pieces straddle N
 }
 ORDERS = [("k", "k"), ("k", "mn"), ("mn", "k"), ("mn", "mn")]
 GUARD = 37
