@@ -85,6 +85,8 @@ __device__ __forceinline__ void lds_write_word(unsigned short* img, int l32, int
   }
 }
 
+#define FP16MC_FRAG_INLINE __attribute__((always_inline))
+
 // The wavefront's LDS writes become visible to its own later reads: LDS
 // executes a wavefront's instructions in order; the wait and the compiler
 // barrier keep the reads of other lanes' words behind the writes.
@@ -134,26 +136,36 @@ frag_copy_kernel(const void* __restrict__ src, void* __restrict__ dst, int64_t g
     u32x4* d = static_cast<u32x4*>(dst) + g0 * (kGroupBytes / 16);
     if (lane < nchunks) in[lane] = __builtin_nontemporal_load(s + lane);
     wave_lds_sync();
-    for (int lg = hw; lg < ng; lg += 2) {
-      if constexpr (DIR == 0) {
-        // image -> the lane's fragment words, lane-major
-        W v;
-#pragma unroll
-        for (int t = 0; t < NUM; ++t) Words<NUM>::set(v, t, lds_read_word<NUM, COL>(in_img + lg * kGroupHalves, l32, t));
-        reinterpret_cast<W*>(out)[lg * 32 + l32] = v;
-      } else if constexpr (DIR == 1) {
-        // the lane's fragment words -> their places in the image
-        const W v = reinterpret_cast<const W*>(in)[lg * 32 + l32];
-#pragma unroll
-        for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out_img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
+    // A lane's words of group lg: read from the source region, then
+    // written to the result region.  In a full block all reads come first
+    // (one wait for all of them), then all writes.
+    auto get = [&](int lg) FP16MC_FRAG_INLINE {
+      W v;
+      if constexpr (DIR == 1) {
+        v = reinterpret_cast<const W*>(in)[lg * 32 + l32];
       } else {
-        // image -> fragment words (registers) -> a second image
-        W v;
 #pragma unroll
         for (int t = 0; t < NUM; ++t) Words<NUM>::set(v, t, lds_read_word<NUM, COL>(in_img + lg * kGroupHalves, l32, t));
+      }
+      return v;
+    };
+    auto put = [&](int lg, const W& v) FP16MC_FRAG_INLINE {
+      if constexpr (DIR == 0) {
+        reinterpret_cast<W*>(out)[lg * 32 + l32] = v;
+      } else {
 #pragma unroll
         for (int t = 0; t < NUM; ++t) lds_write_word<NUM, COL>(out_img + lg * kGroupHalves, l32, t, Words<NUM>::get(v, t));
       }
+    };
+    if (ng == kGroupsPerWave) {
+      constexpr int kIt = kGroupsPerWave / 2;   // groups per half-wave
+      W v[kIt];
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) v[i] = get(hw + 2 * i);
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) put(hw + 2 * i, v[i]);
+    } else {
+      for (int lg = hw; lg < ng; lg += 2) put(lg, get(lg));
     }
     wave_lds_sync();
     if (lane < nchunks) __builtin_nontemporal_store(out[lane], d + lane);
