@@ -368,7 +368,7 @@ def bench_ceilings(torch, stream, a, reps=10):
     i = [0]
 
     def stream():
-        s_, d_ = sets[i[0] % 3]
+        s_, d_ = sets[i[0] % len(sets)]
         i[0] += 1
         if L.ceiling_stream(s_.data_ptr(), d_.data_ptr(), units, rd, wr, sp) != 0:
             raise RuntimeError("ceiling_stream failed")
@@ -376,6 +376,16 @@ def bench_ceilings(torch, stream, a, reps=10):
         stream()
     ms = timer.time(stream, 20)
     res["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
+    del sets
+    # a read stream the size of the skinny product's A (16384 x 32 KiB read, 16 bytes written per unit)
+    units, rd, wr = 16384, 32768, 16
+    sets = [(torch.empty(units * rd // 4, dtype=torch.float32, device="cuda").fill_(1.0),
+             torch.empty(units * wr // 4, dtype=torch.float32, device="cuda")) for _ in range(2)]
+    i = [0]
+    for _ in range(5):
+        stream()
+    ms = timer.time(stream, 20)
+    res["read_16384x32KiB_GB/s"] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
     return res
 
 
@@ -436,6 +446,8 @@ def run_secondary(torch, f, stream, a, b, A, B):
         sec[key]["frac_of_copy"] = round(sec[key]["GB/s"] / copy, 4)
     mix = sec["ceilings"]["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"]
     sec["batched_4096x128x64x64"]["frac_of_same_mix_stream"] = round(sec["batched_4096x128x64x64"]["GB/s"] / mix, 4)
+    rd = sec["ceilings"]["read_16384x32KiB_GB/s"]
+    sec["skinny_16384x8x16384"]["frac_of_read_stream"] = round(sec["skinny_16384x8x16384"]["GB/s"] / rd, 4)
     return sec
 
 
