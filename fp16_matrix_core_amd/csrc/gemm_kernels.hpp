@@ -71,13 +71,24 @@ struct InF16 {
   static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  // The same instruction with the accumulator tied to one AGPR quad, two
-  // wait states after whatever precedes it (a write of the accumulator's
-  // initial value needs them; between MFMAs the matrix pipe is the bound, so
-  // they cost nothing).  The result's read hazard is the caller's: see
+  // The same instruction with the accumulator tied to one AGPR quad.  The
+  // compiler inserts no wait states around inline assembly, so the hazards
+  // are the caller's: mma_tied_nop adds the two wait states that a VALU write
+  // of the accumulator (its zero initialisation) needs before an MFMA reads
+  // it; mma_fresh starts an accumulator from an inline-constant zero C
+  // operand instead, reading no register; after the last MFMA, see
   // tied_mma_fence.
   static __device__ __forceinline__ f32x4 mma_tied(V8 a, V8 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 mma_tied_nop(V8 a, V8 b, f32x4 c) {
     asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 mma_fresh(V8 a, V8 b) {
+    f32x4 c;
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
     return c;
   }
 };
@@ -90,7 +101,16 @@ struct InBF16 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x4 mma_tied(V8 a, V8 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 mma_tied_nop(V8 a, V8 b, f32x4 c) {
     asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 mma_fresh(V8 a, V8 b) {
+    f32x4 c;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
     return c;
   }
 };
@@ -194,7 +214,9 @@ using CfgWg128x64Mn = Cfg<128, 64, 4, 1, 8, 3, 1, 64>;
 // NN and TN spill and TT run 13% slower (accumulators shuffled between
 // AGPRs); those kernels issue the MFMA with tied accumulators instead (see
 // kTied in the kernel): 8192^3 NN 842 -> 789 us, TT 839 -> 791 us, TN 842
-// -> 800 us against 32x32x16.
+// -> 800 us against 32x32x16; without a wait state before every MFMA
+// (interleaved on one box) NN 800 -> 758, TT 799 -> 756, TN 808 -> 760 us,
+// against NT 744 us.
 using CfgWg256 = Cfg<256, 256, 2, 2, 4, 2, 1, 64, 4, 16>;
 // Tall 64x32 tiles for N <= 32: the product streams A (read by one
 // workgroup each, non-temporal) against a B that every workgroup shares.
@@ -572,24 +594,38 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
   // accumulator tied to its AGPRs, which leaves the result-read hazard to
   // tied_mma_fence below.
   constexpr bool kTied = C::MI == 16 && (A_MN || B_MN);
-  auto mfma = [&](const Frags& f, int n) FP16MC_INLINE {
+  // How a tied MFMA meets its accumulator (ignored by the builtin form):
+  // kAfterMfma -- last written by an MFMA, at least a K step earlier;
+  // kFresh -- not yet written: start from zero (the first K step of the
+  // pipelined path); kAfterInit -- just zeroed by the compiler (short K and
+  // the partial slice), two wait states first.
+  enum { kAfterMfma, kFresh, kAfterInit };
+  auto mfma = [&](const Frags& f, int n, auto how) FP16MC_INLINE {
+    constexpr int kHow = decltype(how)::value;
     const int si = n / C::SJ, sj = n % C::SJ;
     const auto& x = kLdsOut ? f.b[sj] : f.a[si];
     const auto& y = kLdsOut ? f.a[si] : f.b[sj];
-    if constexpr (kTied) acc[si][sj] = In::mma_tied(x, y, acc[si][sj]);
-    else acc[si][sj] = In::mma(x, y, acc[si][sj]);
+    if constexpr (!kTied) acc[si][sj] = In::mma(x, y, acc[si][sj]);
+    else if constexpr (kHow == kFresh) acc[si][sj] = In::mma_fresh(x, y);
+    else if constexpr (kHow == kAfterInit) acc[si][sj] = In::mma_tied_nop(x, y, acc[si][sj]);
+    else acc[si][sj] = In::mma_tied(x, y, acc[si][sj]);
   };
+  std::integral_constant<int, kAfterMfma> after_mfma;
+  std::integral_constant<int, kFresh> fresh;
+  std::integral_constant<int, kAfterInit> after_init;
   // The compiler inserts no wait states around an MFMA written as inline
-  // assembly.  Before each one (inside the statement, mma_tied): the zeroes
-  // the compiler writes into the accumulators must have landed before an
-  // MFMA reads them as its C operand (without the wait, elements of the
-  // accumulators that the first MFMAs read came out wrong, varying from run
-  // to run).  After the last one (tied_mma_fence): before anything
-  // other than the next MFMA reads an accumulator, wait longer than the
-  // instruction's result latency (32 wait states, against at most 19 in the
-  // CDNA3 ISA's dependency table), then pass every accumulator through an
-  // empty statement ordered after the wait, so that no read of them can be
-  // scheduled above it.
+  // assembly.  Before the first ones: the zeroes the compiler writes into
+  // the accumulators must have landed before an MFMA reads them as its C
+  // operand (without the wait, elements of the accumulators that the first
+  // MFMAs read came out wrong, varying from run to run); the pipelined path
+  // reads none (kFresh).  Between MFMAs nothing is needed: an accumulator's
+  // next MFMA comes a whole K step later, and a wait state before every MFMA
+  // made the 8192^3 product 4% slower.  After the last one (tied_mma_fence):
+  // before anything other than the next MFMA reads an accumulator, wait
+  // longer than the instruction's result latency (32 wait states, against
+  // at most 19 in the CDNA3 ISA's dependency table), then pass every
+  // accumulator through an empty statement ordered after the wait, so that
+  // no read of them can be scheduled above it.
   auto tied_mma_fence = [&]() FP16MC_INLINE {
     if constexpr (kTied) {
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
@@ -599,7 +635,9 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         for (int sj = 0; sj < C::SJ; ++sj) asm volatile("" : "+a"(acc[si][sj]));
     }
   };
-  auto mfma_all = [&](const Frags& f) FP16MC_INLINE { static_for<NMF>([&](auto n) { mfma(f, decltype(n)::value); }); };
+  auto mfma_all = [&](const Frags& f, auto how) FP16MC_INLINE {
+    static_for<NMF>([&](auto n) { mfma(f, decltype(n)::value, how); });
+  };
   // Wait until at most `n` direct loads of this thread are in flight and its
   // LDS reads/writes are done, then make everyone's writes visible.
   // (A plain s_barrier: a fenced __syncthreads would also wait for the loads
@@ -733,7 +771,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       if constexpr (kPending) {
         static_for<NMF>([&](auto n) {
           constexpr int i = decltype(n)::value;
-          mfma(f1, i);
+          mfma(f1, i, after_mfma);
           if constexpr (i % kRdEvery == 0 && i / kRdEvery < kFrags)
             read_one(as, bs, 0, f0, std::integral_constant<int, i / kRdEvery>{});
           if constexpr (i % kLdEvery == kLdFirst && i / kLdEvery < kLoads)
@@ -752,7 +790,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         static_for<NMF>([&](auto n) {
           constexpr int i = decltype(n)::value;
           constexpr int g = kk * NMF + i;          // MFMA index in the phase
-          mfma(cur, i);
+          mfma(cur, i, std::integral_constant<int, (!kPending && kk == 1) ? kFresh : kAfterMfma>{});
           if constexpr (kPending && g % kLdEvery == kLdFirst && g / kLdEvery < kLoads)
             dma_one(an, bn, next, std::integral_constant<int, g / kLdEvery>{});
           if constexpr (i % kRdEvery == 0 && i / kRdEvery < kFrags)
@@ -764,16 +802,16 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
       return;
     }
     read_frags(as, bs, 0, f0);
-    if constexpr (kPending) mfma_all(f1);
+    if constexpr (kPending) mfma_all(f1, after_mfma);
     dma_all(an, bn, next);
     static_for<KK - 1>([&](auto t) {
       constexpr int kk = decltype(t)::value + 1;
       if constexpr (kk % 2 == 1) {
         read_frags(as, bs, kk, f1);
-        mfma_all(f0);
+        mfma_all(f0, after_mfma);
       } else {
         read_frags(as, bs, kk, f0);
-        mfma_all(f1);
+        mfma_all(f1, after_mfma);
       }
     });
     // Issue order for the scheduler: each step's fragment reads spread between
@@ -816,7 +854,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           read_frags(stage_a(i), stage_b(i), kk, f0);
-          mfma_all(f0);
+          mfma_all(f0, after_init);
         }
       }
     });
@@ -836,7 +874,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
         ++s;
       }
     });
-    mfma_all(f1);  // step (nfull-1, KK-1)
+    mfma_all(f1, after_mfma);  // step (nfull-1, KK-1)
     // drain the idle reloads before any stage is reused or the workgroup ends
     publish_keep(std::integral_constant<int, 0>{});
   }
@@ -857,7 +895,7 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       read_frags(as, bs, kk, f0);
-      mfma_all(f0);
+      mfma_all(f0, after_init);
     }
   }
 
