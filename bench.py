@@ -313,7 +313,7 @@ def ceiling_lib():
     L.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     L.ceiling_copy.restype = ctypes.c_int
     L.ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.ceiling_stream.restype = ctypes.c_int
     return L
 
@@ -361,31 +361,34 @@ def bench_ceilings(torch, stream, a, reps=10):
     res["copy_shapes_GB/s"] = shapes
     res["copy_2^28B_GB/s"] = max(shapes.values())
     del bufs
-    # the batched product's stream: per problem 24 KiB read (A 128x64, B 64x64 fp16), 32 KiB written
-    units, rd, wr = 4096, 24576, 32768
-    sets = [(torch.empty(units * rd // 4, dtype=torch.float32, device="cuda").fill_(1.0),
-             torch.empty(units * wr // 4, dtype=torch.float32, device="cuda")) for _ in range(3)]
-    i = [0]
+    # Streams with the read/write mix of the batched product (per problem 24 KiB
+    # read: A 128x64 and B 64x64 fp16; 32 KiB written) and of the skinny one's A
+    # (32 KiB read per unit), in several launch shapes: one workgroup per unit,
+    # or fewer workgroups taking units in turn, each unit's writes waiting for
+    # its reads (as in the products) or not (overlapped); the best is the ceiling.
+    def stream_ceiling(units, rd, wr, nsets, shapes):
+        sets = [(torch.empty(units * rd // 4, dtype=torch.float32, device="cuda").fill_(1.0),
+                 torch.empty(units * wr // 4, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+        out = {}
+        for grid, overlap in shapes:
+            i = [0]
 
-    def stream():
-        s_, d_ = sets[i[0] % len(sets)]
-        i[0] += 1
-        if L.ceiling_stream(s_.data_ptr(), d_.data_ptr(), units, rd, wr, sp) != 0:
-            raise RuntimeError("ceiling_stream failed")
-    for _ in range(5):
-        stream()
-    ms = timer.time(stream, 20)
-    res["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
-    del sets
-    # a read stream the size of the skinny product's A (16384 x 32 KiB read, 16 bytes written per unit)
-    units, rd, wr = 16384, 32768, 16
-    sets = [(torch.empty(units * rd // 4, dtype=torch.float32, device="cuda").fill_(1.0),
-             torch.empty(units * wr // 4, dtype=torch.float32, device="cuda")) for _ in range(2)]
-    i = [0]
-    for _ in range(5):
-        stream()
-    ms = timer.time(stream, 20)
-    res["read_16384x32KiB_GB/s"] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
+            def stream():
+                s_, d_ = sets[i[0] % nsets]
+                i[0] += 1
+                if L.ceiling_stream(s_.data_ptr(), d_.data_ptr(), units, rd, wr, grid, overlap, sp) != 0:
+                    raise RuntimeError("ceiling_stream failed")
+            for _ in range(5):
+                stream()
+            ms = timer.time(stream, 20)
+            label = f"{'overlapped' if overlap else 'dependent'}_grid{grid if grid else units}"
+            out[label] = round(units * (rd + wr) / (ms * 1e-3) / 1e9, 1)
+        del sets
+        return out, max(out.values())
+    shapes = ((0, 0), (2048, 0), (1536, 1), (2048, 1))
+    res["batched_mix_shapes_GB/s"], res["batched_mix_4096x(24KiB_read+32KiB_write)_GB/s"] = \
+        stream_ceiling(4096, 24576, 32768, 3, shapes)
+    res["read_shapes_GB/s"], res["read_16384x32KiB_GB/s"] = stream_ceiling(16384, 32768, 16, 2, ((0, 0), (4096, 0)))
     return res
 
 

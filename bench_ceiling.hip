@@ -97,18 +97,28 @@ __global__ void __launch_bounds__(T) copy16(const u32x4* __restrict__ src, u32x4
   for (int k = 0; k < D; ++k) __builtin_nontemporal_store(v[k], dst + base + T * k);
 }
 
-// One workgroup per unit: reads rd16 16-byte chunks of its source span and
-// writes wr16 chunks of its destination span (both non-temporal), the
-// written values derived from the read ones so that no load is dropped.
-// The same read/write mix per workgroup as a batched product whose
-// problems each read A and B and write their output once.
+// Units of work that each read rd16 16-byte chunks of their source span and
+// write wr16 chunks of their destination span (both non-temporal), the same
+// read/write mix per unit as a batched product whose problems each read A and
+// B and write their output once.  Workgroups take units grid-stride.  With
+// OVERLAP false a unit's written values derive from its own reads (the
+// product's dependence: its writes wait for its reads); with OVERLAP true
+// they carry the workgroup's previous unit's values, so that a unit's reads
+// and writes can be in flight together.  Either way no load is dropped.
+template <bool OVERLAP>
 __global__ void __launch_bounds__(256) stream_mix(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                  int rd16, int wr16) {
-  const u32x4* s = src + static_cast<int64_t>(blockIdx.x) * rd16;
-  u32x4* d = dst + static_cast<int64_t>(blockIdx.x) * wr16;
-  u32x4 acc = {0u, 0u, 0u, 0u};
-  for (int i = threadIdx.x; i < rd16; i += 256) acc ^= __builtin_nontemporal_load(s + i);
-  for (int i = threadIdx.x; i < wr16; i += 256) __builtin_nontemporal_store(acc + static_cast<unsigned>(i), d + i);
+                                                  int rd16, int wr16, int64_t units) {
+  u32x4 prev = {0u, 0u, 0u, 0u};
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const u32x4* s = src + u * rd16;
+    u32x4* d = dst + u * wr16;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < rd16; i += 256) acc ^= __builtin_nontemporal_load(s + i);
+    const u32x4 w = OVERLAP ? prev : acc;
+    for (int i = threadIdx.x; i < wr16; i += 256) __builtin_nontemporal_store(w + static_cast<unsigned>(i), d + i);
+    prev = acc;
+  }
+  if (OVERLAP && prev[0] == 0x9E3779B9u && prev[1] == 0x7F4A7C15u) dst[threadIdx.x] = prev;  // keep the last reads live
 }
 
 }  // namespace
@@ -147,12 +157,23 @@ int ceiling_copy(const void* src, void* dst, int64_t bytes, int shape, void* str
   return static_cast<int>(hipGetLastError());
 }
 
-// `units` workgroups, each reading rd_bytes from src + u*rd_bytes and writing
-// wr_bytes to dst + u*wr_bytes (both multiples of 16); -1 for bad arguments.
-int ceiling_stream(const void* src, void* dst, int units, int rd_bytes, int wr_bytes, void* stream) {
-  if (units <= 0 || rd_bytes <= 0 || wr_bytes <= 0 || rd_bytes % 16 != 0 || wr_bytes % 16 != 0) return -1;
-  hipLaunchKernelGGL(stream_mix, dim3(units), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), rd_bytes / 16, wr_bytes / 16);
+// `units` units, each reading rd_bytes from src + u*rd_bytes and writing
+// wr_bytes to dst + u*wr_bytes (both multiples of 16), taken by `grid`
+// workgroups (0: one per unit), overlapped or not (see stream_mix); -1 for
+// bad arguments.
+int ceiling_stream(const void* src, void* dst, int units, int rd_bytes, int wr_bytes, int grid, int overlap,
+                   void* stream) {
+  if (units <= 0 || rd_bytes <= 0 || wr_bytes <= 0 || rd_bytes % 16 != 0 || wr_bytes % 16 != 0 || grid < 0 ||
+      wr_bytes < 256 * 16 * (overlap != 0))
+    return -1;
+  const dim3 g(static_cast<unsigned>(grid == 0 || grid > units ? units : grid));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  if (overlap)
+    hipLaunchKernelGGL(stream_mix<true>, g, dim3(256), 0, st, s, d, rd_bytes / 16, wr_bytes / 16, static_cast<int64_t>(units));
+  else
+    hipLaunchKernelGGL(stream_mix<false>, g, dim3(256), 0, st, s, d, rd_bytes / 16, wr_bytes / 16, static_cast<int64_t>(units));
   return static_cast<int>(hipGetLastError());
 }
 

@@ -87,6 +87,7 @@ SHAPES = [
     (100, 5, 64), (77, 16, 200), (33, 17, 70),                 # tall tiles (N <= 32)
     (300, 520, 200), (129, 65, 64), (1000, 999, 136), (2049, 3000, 72),
     (4100, 2050, 100), (4096, 4096, 64), (2304, 4608, 130),    # 128x128 tiles (short K)
+    (4100, 2050, 40),                                          # 128x128, K < 64: the partial slice alone
 ]
 
 
