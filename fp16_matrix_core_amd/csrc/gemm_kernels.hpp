@@ -611,7 +611,6 @@ gemm_nt_kernel(const unsigned short* __restrict__ A, const unsigned short* __res
     else acc[si][sj] = In::mma_tied(x, y, acc[si][sj]);
   };
   std::integral_constant<int, kAfterMfma> after_mfma;
-  std::integral_constant<int, kFresh> fresh;
   std::integral_constant<int, kAfterInit> after_init;
   // The compiler inserts no wait states around an MFMA written as inline
   // assembly.  Before the first ones: the zeroes the compiler writes into
