@@ -430,15 +430,37 @@ def pmc_pass(torch, f):
         "18 x frag_copy")
 
 
+def bench_shards(torch, f, stream, a, b, reps=20):
+    """What one GPU runs when the 8192^3 product is split by rows over P GPUs:
+    A's first 8192/P rows against the whole B (fp16 -> fp32)."""
+    n = 8192
+    res = {}
+    for P in (2, 4, 8):
+        m = n // P
+        o = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+        def call():
+            f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), o.data_ptr(), m, n, n, n, n, n, stream.cuda_stream)
+        for _ in range(20):
+            call()
+        ms = StreamTimer(torch, stream).time(call, reps)
+        tf = 2.0 * m * n * n / ms / 1e9
+        res[f"P{P}_{m}x{n}x{n}"] = {"plan": f.plan(m, n, n), "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2),
+                                     "frac": round(tf / PEAK_TFLOPS, 4)}
+        del o
+    return res
+
+
 def run_secondary(torch, f, stream, a, b, A, B):
-    log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders")
+    log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders, row shards")
     sec = {"ceilings": bench_ceilings(torch, stream, a),
            "frag_copy": bench_frag(torch, f, stream),
            "batched_4096x128x64x64": bench_batched(torch, f, stream),
            "skinny_16384x8x16384": bench_skinny(torch, f, stream),
            "small": bench_small(torch, f, stream),
            "gemm_8192_types": bench_types(torch, f, stream, a, b),
-           "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B)}
+           "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B),
+           "gemm_row_shards": bench_shards(torch, f, stream, a, b)}
     # the bandwidth-bound kernels against what a plain copy moves on this box
     copy = sec["ceilings"]["copy_2^28B_GB/s"]
     fc = sec["frag_copy"]

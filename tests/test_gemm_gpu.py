@@ -188,6 +188,21 @@ def test_large_square_every_element(f):
     check_all_rows(out, lambda r0, r1: oracle.gemm_nt(A[r0:r1], B))
 
 
+def test_row_shard_every_element(f):
+    """A's first 1024 rows against the whole 8192 x 8192 B (what each of 8 GPUs
+    would run with the product split by rows), through a 1032-row buffer whose
+    last 8 rows must stay untouched; every element checked."""
+    A, B = inputs.large_square()
+    a, b = _dev(A), _dev(B)
+    m, n = 1024, 8192
+    buf = torch.full((m + 8, n), SENTINEL, dtype=torch.float32, device="cuda")
+    f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), buf.data_ptr(), m, n, n, n, n, n,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf[m:]).all()), "rows past M written"
+    check_all_rows(buf[:m], lambda r0, r1: oracle.gemm_nt(A[r0:r1], B))
+
+
 def test_batched_small(f):
     """4096 independent 128x64 by 64x64 problems (seed 5), one launch; every element checked."""
     A, B = inputs.batched_small()
