@@ -451,8 +451,29 @@ def bench_shards(torch, f, stream, a, b, reps=20):
     return res
 
 
+def bench_library(torch, stream, a, b, reps=20):
+    """Context, not a ceiling: the vendor BLAS behind torch.mm on the same 8192^3
+    fp16 operands (fp16 output, the only output type torch.mm gives for fp16
+    operands; compare gemm_8192_types.f16_in_f16_out). B is passed as a
+    contiguous K x N copy of its transpose."""
+    n = 8192
+    x = a.view(torch.float16)
+    y = b.view(torch.float16).t().contiguous()
+    o = torch.empty((n, n), dtype=torch.float16, device="cuda")
+
+    def call():
+        torch.mm(x, y, out=o)
+    for _ in range(20):
+        call()
+    ms = StreamTimer(torch, stream).time(call, reps)
+    tf = 2.0 * n ** 3 / ms / 1e9
+    del y, o
+    return {"torch_mm_f16_in_f16_out_8192": {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2),
+                                              "frac": round(tf / PEAK_TFLOPS, 4)}}
+
+
 def run_secondary(torch, f, stream, a, b, A, B):
-    log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders, row shards")
+    log("secondary: ceilings, frag_copy, batched, skinny, small, operand/output types, storage orders, row shards, vendor BLAS")
     sec = {"ceilings": bench_ceilings(torch, stream, a),
            "frag_copy": bench_frag(torch, f, stream),
            "batched_4096x128x64x64": bench_batched(torch, f, stream),
@@ -460,7 +481,8 @@ def run_secondary(torch, f, stream, a, b, A, B):
            "small": bench_small(torch, f, stream),
            "gemm_8192_types": bench_types(torch, f, stream, a, b),
            "gemm_8192_storage_orders": bench_layouts(torch, f, stream, A, B),
-           "gemm_row_shards": bench_shards(torch, f, stream, a, b)}
+           "gemm_row_shards": bench_shards(torch, f, stream, a, b),
+           "vendor_blas": bench_library(torch, stream, a, b)}
     # the bandwidth-bound kernels against what a plain copy moves on this machine
     copy = sec["ceilings"]["copy_2^28B_GB/s"]
     fc = sec["frag_copy"]

@@ -1,13 +1,16 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python bench_profile.py stats   --csv KERNEL_STATS.csv --match SUBSTR --command CMD --out FILE
+    python bench_profile.py stats   --csv KERNEL_STATS.csv [--match SUBSTR] --command CMD --out FILE
+    python bench_profile.py stats   --by-grid --csv KERNEL_TRACE.csv --command CMD --out FILE
     python bench_profile.py traffic --fetch FETCH.csv --write WRITE.csv --match SUBSTR
                                    --command CMD --out FILE
     python bench_profile.py counters --csv PASS1.csv [--csv PASS2.csv ...] --kernel LABEL=SUBSTR
                                      [--skip N] --command CMD --out FILE
 
 ``stats`` condenses a ``--kernel-trace --stats`` kernel_stats.csv to the
-kernels' call counts and average durations.  ``counters`` averages the
+kernels' call counts and average durations (with ``--by-grid``, the
+kernel_trace.csv of the same run, one row per kernel and grid size, so that
+one kernel launched at several shapes is not averaged across them).  ``counters`` averages the
 counters of one or more ``--pmc`` passes per kernel and derives the clock,
 the MFMA busy fraction and the LDS bank-conflict rate.  ``traffic`` turns two
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` counter_collection.csv files into
@@ -77,6 +80,21 @@ def kernel_stats(path, match=None):
         out.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                     "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])})
     return out
+
+
+def kernel_stats_by_grid(path, match=None):
+    """The same figures from a kernel_trace.csv, one row per kernel and grid size
+    (launches of one kernel at different shapes stay apart)."""
+    groups = {}
+    for r in _rows(path):
+        if match and match not in r["Kernel_Name"]:
+            continue
+        wgs = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(
+            1, int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault((r["Kernel_Name"], wgs), []).append(ns)
+    return [{"name": name, "workgroups": wgs, "calls": len(v), "avg_ns": sum(v) / len(v),
+             "min_ns": float(min(v)), "max_ns": float(max(v))} for (name, wgs), v in groups.items()]
 
 
 def counter_per_dispatch(path, match):
@@ -162,7 +180,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
-    s.add_argument("--csv", required=True)
+    s.add_argument("--csv", required=True, help="kernel_stats.csv, or kernel_trace.csv with --by-grid")
+    s.add_argument("--by-grid", action="store_true", help="--csv is a kernel_trace.csv: one row per grid size")
     s.add_argument("--match", default=None)
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
@@ -188,13 +207,17 @@ def main(argv=None):
     a = ap.parse_args(argv)
     stamp = time.strftime("%Y-%m-%d")
     if a.cmd == "stats":
-        ks = kernel_stats(a.csv, a.match)
+        ks = kernel_stats_by_grid(a.csv, a.match) if a.by_grid else kernel_stats(a.csv, a.match)
         lines = [f"# rocprofv3 kernel statistics ({stamp})", f"# command: {a.command}",
                  "# gemm_nt_kernel<tile configuration, operand type, output type, accumulate,"
-                 " A stored K x M, B stored K x N>", "",
-                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+                 " A stored K x M, B stored K x N>", ""]
+        if a.by_grid:
+            lines += ["| kernel | workgroups | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        else:
+            lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for k in sorted(ks, key=lambda k: -k["avg_ns"] * k["calls"]):
-            lines.append(f"| `{short_name(k['name'])[:160]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
+            grid = f" {k['workgroups']} |" if a.by_grid else ""
+            lines.append(f"| `{short_name(k['name'])[:160]}` |{grid} {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
                          f"{k['min_ns'] / 1e3:.2f} | {k['max_ns'] / 1e3:.2f} |")
         text = "\n".join(lines) + "\n"
     elif a.cmd == "counters":
