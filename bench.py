@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -131,11 +132,13 @@ def cpu_baseline(A, B, target_s=10.0):
             "sample": f"rows 0..{rows - 1} of the 8192^3 product (ref and |A||B| bound, float64), {dt:.1f} s"}
 
 
-def bench_frag(torch, f, stream, reps=20, sets=3):
+def bench_frag(torch, f, stream, reps=20, sets=3, rounds=3):
     """frag_copy GB/s over 2^20 tiles (256 MiB moved per call).
 
     cold: three rotating buffer sets (768 MiB, more than the last-level cache
     holds, so every call streams from HBM); warm: one set called repeatedly.
+    Each of the 18 combinations is timed once per round, the rounds sweeping
+    all of them in turn, and reported as its median over the rounds.
     """
     from fp16_matrix_core_amd import inputs
     n_tiles = inputs.FRAG_TILES
@@ -144,25 +147,28 @@ def bench_frag(torch, f, stream, reps=20, sets=3):
     srcs = [bits.clone() for _ in range(sets)]
     dsts = [torch.empty_like(bits) for _ in range(sets)]
     timer = StreamTimer(torch, stream)
-    cold, warm = {}, {}
-    for num in (1, 2, 4):
-        for col in (0, 1):
-            for direction, dname in ((0, "load"), (1, "store"), (2, "roundtrip")):
-                name = f"num{num}_{'col' if col else 'row'}_{dname}"
-                for res, nsets in ((cold, sets), (warm, 1)):
-                    i = [0]
+    runs = {}
+    for _ in range(rounds):
+        for num in (1, 2, 4):
+            for col in (0, 1):
+                for direction, dname in ((0, "load"), (1, "store"), (2, "roundtrip")):
+                    name = f"num{num}_{'col' if col else 'row'}_{dname}"
+                    for kind, nsets in (("cold", sets), ("warm", 1)):
+                        i = [0]
 
-                    def call():
-                        k = i[0] % nsets
-                        i[0] += 1
-                        f.frag_copy_raw(srcs[k].data_ptr(), dsts[k].data_ptr(), n_tiles, num, col, direction,
-                                        stream.cuda_stream)
-                    for _ in range(3):
-                        call()
-                    ms = timer.time(call, reps)
-                    res[name] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+                        def call():
+                            k = i[0] % nsets
+                            i[0] += 1
+                            f.frag_copy_raw(srcs[k].data_ptr(), dsts[k].data_ptr(), n_tiles, num, col, direction,
+                                            stream.cuda_stream)
+                        for _ in range(3):
+                            call()
+                        ms = timer.time(call, reps)
+                        runs.setdefault((kind, name), []).append(2 * nbytes / (ms * 1e-3) / 1e9)
+    cold = {name: round(statistics.median(v), 1) for (kind, name), v in runs.items() if kind == "cold"}
+    warm = {name: round(statistics.median(v), 1) for (kind, name), v in runs.items() if kind == "warm"}
     vals = list(cold.values())
-    return {"unit": "GB/s", "bytes_per_call": 2 * nbytes, "peak": PEAK_HBM_GBS,
+    return {"unit": "GB/s", "bytes_per_call": 2 * nbytes, "peak": PEAK_HBM_GBS, "rounds": rounds,
             "min_frac": round(min(vals) / PEAK_HBM_GBS, 4), "max_frac": round(max(vals) / PEAK_HBM_GBS, 4),
             "results": cold, "warm": warm}
 
