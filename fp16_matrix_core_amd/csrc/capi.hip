@@ -68,6 +68,10 @@ int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t
   if (!live) return FP16MC_OK;
   if (K > 0 && (A == nullptr || B == nullptr)) return fail(FP16MC_EINVAL, "A or B is NULL");
   if (Out == nullptr) return fail(FP16MC_EINVAL, "Out is NULL");
+  // Problems that shared output cells would race on them.
+  if (batch > 1 && sO < (M - 1) * ldo + N)
+    return fail(FP16MC_EINVAL, "strideO=%lld lets the problems' outputs overlap (at least (M-1)*ldo+N = %lld)",
+                (long long)sO, (long long)((M - 1) * ldo + N));
   if (!aligned16(A) || !aligned16(B))
     return fail(FP16MC_EALIGN, "A and B must be 16-byte aligned (8 fp16 per access)");
   if ((lda & 7) || (ldb & 7))

@@ -73,8 +73,9 @@ int gemm_nt_f16f32(const void* A, const void* B, float* Out,
  * A + b*strideA, B + b*strideB, Out + b*strideO (strides in elements) with
  * the shapes and row strides above.  Same preconditions per problem, plus
  * batch >= 0, strides >= 0, strideA and strideB multiples of 8, strideO a
- * multiple of 4.  batch == 1 is exactly gemm_nt_f16f32.  The problems'
- * output ranges must not overlap.
+ * multiple of 4.  batch == 1 is exactly gemm_nt_f16f32.  The operands may be
+ * shared between problems (strideA or strideB 0); the outputs may not
+ * overlap: with batch > 1, strideO >= (M-1)*ldo + N (else FP16MC_EINVAL).
  */
 int gemm_nt_f16f32_batched(const void* A, const void* B, float* Out,
                            int64_t M, int64_t N, int64_t K,

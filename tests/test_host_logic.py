@@ -97,6 +97,18 @@ def test_gemm_batched_validation(L):
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, -8, 128, 64, None) == -1
 
 
+def test_gemm_batched_outputs_may_not_overlap(L):
+    # M = 8 rows of N = 8 at ldo = 8: a problem's output spans 64 elements
+    for so in (0, 8, 60):
+        assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 128, 128, so, None) == -1
+        assert "overlap" in L.fp16mc_last_error().decode()
+    # with ldo = 12 the last row ends at 7*12 + 8 = 92 elements
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 12, 2, 128, 128, 88, None) == -1
+    # shared operands (strides 0) do not excuse overlapping outputs
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 0, 0, 30, None) == -1
+    assert "overlap" in L.fp16mc_last_error().decode()
+
+
 # gemm_nt_ex(A, B, Out, M, N, K, lda, ldb, ldo, batch, sA, sB, sO, ab_type, out_type, accumulate)
 EX_OK = (FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1, 0, 0, 0)
 
