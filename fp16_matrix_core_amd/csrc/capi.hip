@@ -149,6 +149,13 @@ int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_ma
   if (num_tiles == 0) return ok();
   if (src == nullptr || dst == nullptr) return fail(FP16MC_EINVAL, "src or dst is NULL");
   if (!aligned16(src) || !aligned16(dst)) return fail(FP16MC_EALIGN, "src and dst must be 16-byte aligned");
+  // Each wavefront reads a whole block before writing the same block, so
+  // src == dst works; a partial overlap would let one wavefront overwrite
+  // what another has yet to read.
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = static_cast<uintptr_t>(num_tiles) * 128u;
+  if (s0 != d0 && s0 < d0 + bytes && d0 < s0 + bytes)
+    return fail(FP16MC_EINVAL, "src and dst overlap without being the same buffer");
   const hipError_t e = fp16mc::launch_frag_copy(src, dst, num_tiles / num, num, col_major != 0, direction,
                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP16MC_EHIP, "launch failed: %s", hipGetErrorString(e));

@@ -196,9 +196,11 @@ enum {
  * payloads, infinities, subnormals and -0 are preserved exactly.
  *
  * src, dst: device pointers, 16-byte aligned (else FP16MC_EALIGN), each
- *   num_tiles*128 bytes, not overlapping.  LOAD reads an image and writes a
- *   fragment; STORE the reverse; ROUNDTRIP reads an image and writes the
- *   image it reconstructs from the fragment (bit-identical to src).
+ *   num_tiles*128 bytes; either the same buffer (the transfer is done in
+ *   place) or not overlapping at all (else FP16MC_EINVAL).  LOAD reads an
+ *   image and writes a fragment; STORE the reverse; ROUNDTRIP reads an image
+ *   and writes the image it reconstructs from the fragment (bit-identical to
+ *   src).
  * num_tiles >= 0 and a multiple of num; num in {1,2,4}; col_major in {0,1};
  *   direction one of FRAG_*  (else FP16MC_EINVAL).  num_tiles == 0: no-op.
  */

@@ -102,3 +102,22 @@ def test_torch_binding(f):
     f.frag_copy(src, dst, 2, True, LOAD)
     torch.cuda.synchronize()
     assert np.array_equal(dst.cpu().numpy().view(np.uint32), oracle.frag_load(img, 2, True))
+
+
+@pytest.mark.parametrize("num", [1, 2, 4])
+@pytest.mark.parametrize("col", [0, 1], ids=["row", "col"])
+def test_in_place(f, num, col):
+    """src == dst: each direction gives what it gives out of place (a whole-block
+    count and a ragged one, so a partial last block is covered too)."""
+    for groups in (4096, 4099):
+        rng = np.random.default_rng(500 + 10 * num + col + groups)
+        img = inputs.random_bits_u16(groups * 64 * num, rng)
+        for direction, want in ((LOAD, oracle.frag_load(img, num, col)),
+                                (STORE, oracle.frag_store(img.view(np.uint32), num, col)),
+                                (ROUNDTRIP, img)):
+            buf = torch.from_numpy(img.view(np.uint8).copy()).cuda()
+            f.frag_copy_raw(buf.data_ptr(), buf.data_ptr(), groups * num, num, col, direction,
+                            torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            got = buf.cpu().numpy()
+            assert np.array_equal(got, np.ascontiguousarray(want).view(np.uint8)), (groups, direction)

@@ -202,6 +202,8 @@ def test_empty_problems_enqueue_nothing(L):
     ((FAKE, FAKE, 8, 2, 0, 3), -1, "direction"),
     ((0, FAKE, 8, 2, 0, 0), -1, "NULL"),
     ((MISALIGNED, FAKE, 8, 2, 0, 1), -2, "16-byte aligned"),
+    ((FAKE, FAKE + 512, 8, 2, 0, 0), -1, "overlap"),          # 8 tiles = 1 KiB: dst starts inside src
+    ((FAKE + 1008, FAKE, 8, 2, 0, 2), -1, "overlap"),         # dst's last 16 bytes are src's first
 ])
 def test_frag_copy_validation(L, args, code, needle):
     assert L.frag_copy(*args, None) == code
