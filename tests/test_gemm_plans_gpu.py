@@ -66,8 +66,21 @@ def _stored(X, order, fmt):
 @pytest.mark.parametrize("ab,out_fmt,acc", TYPES)
 def test_plan(f, plan, a_order, b_order, ab, out_fmt, acc):
     M, N, K = PLAN_SHAPES[plan]
+    _check_case(f, plan, M, N, K, a_order, b_order, ab, out_fmt, acc)
+
+
+@pytest.mark.parametrize("K", [3136, 3140], ids=["49_slices", "49_slices_and_4"])
+@pytest.mark.parametrize("a_order,b_order", ORDERS)
+@pytest.mark.parametrize("ab,out_fmt,acc", TYPES)
+def test_wg256x256_odd_slice_count(f, K, a_order, b_order, ab, out_fmt, acc):
+    """The 256x256 K loop with an odd number of whole slices (no trailing phase
+    after the paired ones), with and without a partial slice after them."""
+    _check_case(f, "wg256x256", 4100, 2200, K, a_order, b_order, ab, out_fmt, acc)
+
+
+def _check_case(f, plan, M, N, K, a_order, b_order, ab, out_fmt, acc):
     assert f.plan_ex(M, N, K, 1, ORDER[a_order], ORDER[b_order]).split("_")[0] == plan
-    rng = np.random.default_rng(zlib.crc32(f"{plan}/{a_order}/{b_order}/{ab}".encode()))
+    rng = np.random.default_rng(zlib.crc32(f"{plan}/{M}x{N}x{K}/{a_order}/{b_order}/{ab}".encode()))
     draw = inputs.uniform_f16 if ab == "f16" else inputs.uniform_bf16
     A = draw((M, K), rng)
     B = draw((N, K), rng)
