@@ -69,9 +69,15 @@ int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t
   if (K > 0 && (A == nullptr || B == nullptr)) return fail(FP16MC_EINVAL, "A or B is NULL");
   if (Out == nullptr) return fail(FP16MC_EINVAL, "Out is NULL");
   // Problems that shared output cells would race on them.
-  if (batch > 1 && sO < (M - 1) * ldo + N)
-    return fail(FP16MC_EINVAL, "strideO=%lld lets the problems' outputs overlap (at least (M-1)*ldo+N = %lld)",
-                (long long)sO, (long long)((M - 1) * ldo + N));
+  if (batch > 1) {
+    int64_t span = 0;
+    if (__builtin_mul_overflow(M - 1, ldo, &span) || __builtin_add_overflow(span, N, &span))
+      return fail(FP16MC_EINVAL, "M=%lld rows of ldo=%lld elements overflow 64-bit offsets", (long long)M,
+                  (long long)ldo);
+    if (sO < span)
+      return fail(FP16MC_EINVAL, "strideO=%lld lets the problems' outputs overlap (at least (M-1)*ldo+N = %lld)",
+                  (long long)sO, (long long)span);
+  }
   if (!aligned16(A) || !aligned16(B))
     return fail(FP16MC_EALIGN, "A and B must be 16-byte aligned (8 fp16 per access)");
   if ((lda & 7) || (ldb & 7))
@@ -153,8 +159,11 @@ int frag_copy(const void* src, void* dst, int64_t num_tiles, int num, int col_ma
   // src == dst works; a partial overlap would let one wavefront overwrite
   // what another has yet to read.
   const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
-  const uintptr_t bytes = static_cast<uintptr_t>(num_tiles) * 128u;
-  if (s0 != d0 && s0 < d0 + bytes && d0 < s0 + bytes)
+  uintptr_t bytes = 0, s_end = 0, d_end = 0;
+  if (__builtin_mul_overflow(static_cast<uintptr_t>(num_tiles), uintptr_t(128), &bytes) ||
+      __builtin_add_overflow(s0, bytes, &s_end) || __builtin_add_overflow(d0, bytes, &d_end))
+    return fail(FP16MC_EINVAL, "num_tiles=%lld spans past the end of the address space", (long long)num_tiles);
+  if (s0 != d0 && s0 < d_end && d0 < s_end)
     return fail(FP16MC_EINVAL, "src and dst overlap without being the same buffer");
   const hipError_t e = fp16mc::launch_frag_copy(src, dst, num_tiles / num, num, col_major != 0, direction,
                                                 static_cast<hipStream_t>(stream));

@@ -88,18 +88,28 @@ const char* gemm_plan_name(GemmPlan plan, bool a_mn, bool b_mn) {
   }
 }
 
+// Workgroups of the launch, saturated at INT64_MAX instead of wrapping (the
+// caller rejects anything above its grid limit).
+template <class C>
+int64_t grid_of(int64_t M, int64_t N, int64_t batch) {
+  const int64_t tm = M / C::BM + (M % C::BM != 0);
+  const int64_t tn = N / C::BN + (N % C::BN != 0);
+  int64_t t = 0;
+  if (__builtin_mul_overflow(tm, tn, &t) || __builtin_mul_overflow(t, batch, &t)) return INT64_MAX;
+  return t;
+}
+
 int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
-  int64_t tm, tn;
   switch (plan) {
-    case GemmPlan::kWave32: return tiles_of<CfgWave32>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg128x64: return tiles_of<CfgWg128x64>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg256: return tiles_of<CfgWg256>(M, N, batch, &tm, &tn);
-    case GemmPlan::kTall: return tiles_of<CfgTall>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg128x64Stream: return tiles_of<CfgWg128x64Stream>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg256x128: return tiles_of<CfgWg256x128>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg128x128: return tiles_of<CfgWg128x128>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWide: return tiles_of<CfgWide>(M, N, batch, &tm, &tn);
-    case GemmPlan::kWg64: return tiles_of<CfgWg64>(M, N, batch, &tm, &tn);
+    case GemmPlan::kWave32: return grid_of<CfgWave32>(M, N, batch);
+    case GemmPlan::kWg128x64: return grid_of<CfgWg128x64>(M, N, batch);
+    case GemmPlan::kWg256: return grid_of<CfgWg256>(M, N, batch);
+    case GemmPlan::kTall: return grid_of<CfgTall>(M, N, batch);
+    case GemmPlan::kWg128x64Stream: return grid_of<CfgWg128x64Stream>(M, N, batch);
+    case GemmPlan::kWg256x128: return grid_of<CfgWg256x128>(M, N, batch);
+    case GemmPlan::kWg128x128: return grid_of<CfgWg128x128>(M, N, batch);
+    case GemmPlan::kWide: return grid_of<CfgWide>(M, N, batch);
+    case GemmPlan::kWg64: return grid_of<CfgWg64>(M, N, batch);
     default: return 0;
   }
 }
@@ -110,6 +120,8 @@ int64_t gemm_plan_grid(GemmPlan plan, int64_t M, int64_t N, int64_t batch) {
 template <class C>
 bool fits_offsets(int64_t K, int64_t lda, int64_t ldb, int64_t ldo, int64_t out_bytes, bool a_mn, bool b_mn) {
   const int64_t limit = int64_t(1) << 32;
+  // Larger values fail below anyway; bounding them first keeps the products in range.
+  if (K >= limit || lda >= limit || ldb >= limit || ldo >= (int64_t(1) << 31)) return false;
   const int64_t a = a_mn ? 2 * C::BK * lda : 2 * ((C::BM - 1) * lda + K);
   const int64_t b = b_mn ? 2 * C::BK * ldb : 2 * ((C::BN - 1) * ldb + K);
   // Out is addressed from each tile's origin with signed 32-bit row offsets

@@ -97,6 +97,20 @@ def test_gemm_batched_validation(L):
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, -8, 128, 64, None) == -1
 
 
+def test_huge_sizes_are_refused_not_wrapped(L):
+    # sizes whose tile counts or byte offsets would overflow 64-bit arithmetic
+    big = 1 << 62
+    assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, big, big, 16, 16, 16, big, None) == -1
+    assert "workgroups" in L.fp16mc_last_error().decode()
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 1 << 40, 1 << 40, 16, 16, 16, 1 << 40, 1, 0, 0, 0,
+                                    None) == -1
+    assert "workgroups" in L.fp16mc_last_error().decode()
+    assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, 4096, 4096, 16, 1 << 60, 16, 4096, None) == -1
+    assert "2^32" in L.fp16mc_last_error().decode()
+    assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, 4096, 4096, 16, 16, 16, 1 << 61, None) == -1
+    assert "2^31" in L.fp16mc_last_error().decode()
+
+
 def test_gemm_batched_outputs_may_not_overlap(L):
     # M = 8 rows of N = 8 at ldo = 8: a problem's output spans 64 elements
     for so in (0, 8, 60):
@@ -107,6 +121,10 @@ def test_gemm_batched_outputs_may_not_overlap(L):
     # shared operands (strides 0) do not excuse overlapping outputs
     assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 0, 0, 30, None) == -1
     assert "overlap" in L.fp16mc_last_error().decode()
+    # an output span past 64-bit offsets is refused, not wrapped
+    big = 1 << 40
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, big, 8, 16, 16, 16, big, 2, 0, 0, 0, None) == -1
+    assert "overflow" in L.fp16mc_last_error().decode()
 
 
 # gemm_nt_ex(A, B, Out, M, N, K, lda, ldb, ldo, batch, sA, sB, sO, ab_type, out_type, accumulate)
@@ -204,6 +222,7 @@ def test_empty_problems_enqueue_nothing(L):
     ((MISALIGNED, FAKE, 8, 2, 0, 1), -2, "16-byte aligned"),
     ((FAKE, FAKE + 512, 8, 2, 0, 0), -1, "overlap"),          # 8 tiles = 1 KiB: dst starts inside src
     ((FAKE + 1008, FAKE, 8, 2, 0, 2), -1, "overlap"),         # dst's last 16 bytes are src's first
+    ((FAKE, FAKE, 1 << 60, 4, 0, 0), -1, "address space"),    # 2^67 bytes
 ])
 def test_frag_copy_validation(L, args, code, needle):
     assert L.frag_copy(*args, None) == code
