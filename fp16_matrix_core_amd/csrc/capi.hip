@@ -68,6 +68,14 @@ int check_gemm(const void* A, const void* B, const void* Out, int64_t M, int64_t
   if (!live) return FP16MC_OK;
   if (K > 0 && (A == nullptr || B == nullptr)) return fail(FP16MC_EINVAL, "A or B is NULL");
   if (Out == nullptr) return fail(FP16MC_EINVAL, "Out is NULL");
+  if (batch > 1) {
+    // Problem b starts b * stride elements in: the last one's byte offset must be representable.
+    const int64_t s_ab = sA > sB ? sA : sB;
+    int64_t last = 0;
+    if (__builtin_mul_overflow(batch - 1, s_ab, &last) || __builtin_mul_overflow(last, int64_t(2), &last) ||
+        __builtin_mul_overflow(batch - 1, sO, &last) || __builtin_mul_overflow(last, int64_t(4), &last))
+      return fail(FP16MC_EINVAL, "batch=%lld with these strides overflows 64-bit offsets", (long long)batch);
+  }
   // Problems that shared output cells would race on them.
   if (batch > 1) {
     int64_t span = 0;

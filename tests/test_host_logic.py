@@ -109,6 +109,8 @@ def test_huge_sizes_are_refused_not_wrapped(L):
     assert "2^32" in L.fp16mc_last_error().decode()
     assert L.gemm_nt_f16f32(FAKE, FAKE, FAKE, 4096, 4096, 16, 16, 16, 1 << 61, None) == -1
     assert "2^31" in L.fp16mc_last_error().decode()
+    assert L.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1 << 20, 1 << 50, 0, 64, None) == -1
+    assert "overflows" in L.fp16mc_last_error().decode()
 
 
 def test_gemm_batched_outputs_may_not_overlap(L):
