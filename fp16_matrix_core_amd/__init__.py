@@ -14,7 +14,12 @@ every entry point raises if the library is not built.
     frag_copy(src, dst, num, col_major, direction)
     plan(M, N, K, batch=1)         name of the kernel configuration used
 
-C ABI names and status codes are those of include/fp16mc.h.
+Pointer-level calls with the C ABI's names and argument order (integer
+device pointers, the stream as an integer handle): gemm_nt_f16f32,
+gemm_nt_f16f32_batched, gemm_nt_ex, gemm_ex, frag_copy_raw (the C frag_copy),
+gemm_nt_f16f32_plan, gemm_ex_plan.  Status codes are those of
+include/fp16mc.h; a nonzero status raises Fp16mcError with the library's
+message.
 """
 
 import ctypes
@@ -24,6 +29,7 @@ __all__ = [
     "FRAG_LOAD", "FRAG_STORE", "FRAG_ROUNDTRIP", "Fp16mcError", "lib", "lib_path",
     "gemm_nt", "gemm_nt_batched", "frag_copy", "plan", "gemm_nt_raw", "gemm_nt_ex_raw", "frag_copy_raw",
     "F32", "F16", "BF16", "K_CONTIGUOUS", "MN_CONTIGUOUS", "matmul", "gemm_ex_raw", "plan_ex",
+    "gemm_nt_f16f32", "gemm_nt_f16f32_batched", "gemm_nt_ex", "gemm_ex", "gemm_nt_f16f32_plan", "gemm_ex_plan",
 ]
 
 FRAG_LOAD, FRAG_STORE, FRAG_ROUNDTRIP = 0, 1, 2
@@ -130,7 +136,44 @@ def gemm_ex_raw(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch=1, sa=0, sb
 
 
 def frag_copy_raw(src_ptr, dst_ptr, num_tiles, num, col_major, direction, stream=0):
+    """Direct call of frag_copy with integer device pointers."""
     _check(lib().frag_copy(src_ptr, dst_ptr, num_tiles, num, int(col_major), direction, stream))
+
+
+def gemm_nt_f16f32(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream=0):
+    """gemm_nt_f16f32 of the C ABI (integer device pointers)."""
+    _check(lib().gemm_nt_f16f32(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, stream))
+
+
+def gemm_nt_f16f32_batched(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a, stride_b, stride_o,
+                           stream=0):
+    """gemm_nt_f16f32_batched of the C ABI (integer device pointers, strides in elements)."""
+    _check(lib().gemm_nt_f16f32_batched(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a,
+                                        stride_b, stride_o, stream))
+
+
+def gemm_nt_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a, stride_b, stride_o, ab_type,
+               out_type, accumulate, stream=0):
+    """gemm_nt_ex of the C ABI (integer device pointers)."""
+    _check(lib().gemm_nt_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a, stride_b, stride_o,
+                            ab_type, out_type, int(accumulate), stream))
+
+
+def gemm_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a, stride_b, stride_o, a_order, b_order,
+            ab_type, out_type, accumulate, stream=0):
+    """gemm_ex of the C ABI (integer device pointers)."""
+    _check(lib().gemm_ex(a_ptr, b_ptr, out_ptr, M, N, K, lda, ldb, ldo, batch, stride_a, stride_b, stride_o,
+                         a_order, b_order, ab_type, out_type, int(accumulate), stream))
+
+
+def gemm_nt_f16f32_plan(M, N, K, batch=1):
+    """gemm_nt_f16f32_plan of the C ABI: the kernel configuration's name, or None."""
+    return plan(M, N, K, batch)
+
+
+def gemm_ex_plan(M, N, K, batch=1, a_order=K_CONTIGUOUS, b_order=K_CONTIGUOUS):
+    """gemm_ex_plan of the C ABI."""
+    return plan_ex(M, N, K, batch, a_order, b_order)
 
 
 def _types(a, b, out_dtype):

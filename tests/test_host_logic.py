@@ -51,6 +51,36 @@ def test_exports_every_declared_symbol(L):
         assert re.search(rf"\bT {n}$", nm, flags=re.M), f"{n} is not a defined text symbol"
 
 
+def test_binding_has_every_entry_point_by_its_c_name():
+    """The Python binding offers each declared function under its C name (frag_copy's
+    pointer-level form is frag_copy_raw; fp16mc_last_error feeds the exceptions)."""
+    import inspect
+    import fp16_matrix_core_amd as f
+    for n in _declared_functions():
+        if n == "fp16mc_last_error":
+            continue
+        py = "frag_copy_raw" if n == "frag_copy" else n
+        assert callable(getattr(f, py, None)), f"binding lacks {py}"
+    # pointer-level functions take the C arguments in the C order (stream last, optional)
+    assert list(inspect.signature(f.gemm_nt_f16f32).parameters)[:9] == \
+        ["a_ptr", "b_ptr", "out_ptr", "M", "N", "K", "lda", "ldb", "ldo"]
+    assert list(inspect.signature(f.gemm_ex).parameters)[-1] == "stream"
+
+
+def test_binding_c_names_validate_like_the_library(L):
+    import fp16_matrix_core_amd as f
+    with pytest.raises(f.Fp16mcError, match="lda=8 < K=16"):
+        f.gemm_nt_f16f32(FAKE, FAKE, FAKE, 8, 8, 16, 8, 16, 8)
+    with pytest.raises(f.Fp16mcError, match="overlap"):
+        f.gemm_nt_f16f32_batched(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 2, 128, 128, 0)
+    with pytest.raises(f.Fp16mcError, match="ab_type=3"):
+        f.gemm_nt_ex(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1, 0, 0, 0, 3, 0, 0)
+    with pytest.raises(f.Fp16mcError, match="a_order=2"):
+        f.gemm_ex(FAKE, FAKE, FAKE, 8, 8, 16, 16, 16, 8, 1, 0, 0, 0, 2, 0, 1, 0, 0)
+    assert f.gemm_nt_f16f32_plan(8192, 8192, 8192) == L.gemm_nt_f16f32_plan(8192, 8192, 8192, 1).decode()
+    assert f.gemm_ex_plan(8192, 8192, 8192, 1, 1, 1) == L.gemm_ex_plan(8192, 8192, 8192, 1, 1, 1).decode()
+
+
 FAKE = 0x1000       # never dereferenced: every call below fails validation first
 MISALIGNED = 0x1002
 
