@@ -182,8 +182,8 @@ def test_large_square_every_element(f):
     a, b = _dev(A), _dev(B)
     out = torch.full((8192, 8192), SENTINEL, dtype=torch.float32, device="cuda")
     assert f.plan(8192, 8192, 8192).startswith("wg256")
-    f.gemm_nt_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), 8192, 8192, 8192, 8192, 8192, 8192,
-                  torch.cuda.current_stream().cuda_stream)
+    f.gemm_nt_f16f32(a.data_ptr(), b.data_ptr(), out.data_ptr(), 8192, 8192, 8192, 8192, 8192, 8192,
+                     torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     check_all_rows(out, lambda r0, r1: oracle.gemm_nt(A[r0:r1], B))
 
@@ -204,14 +204,22 @@ def test_row_shard_every_element(f):
 
 
 def test_batched_small(f):
-    """4096 independent 128x64 by 64x64 problems (seed 5), one launch; every element checked."""
+    """4096 independent 128x64 by 64x64 problems (seed 5), one launch; every element checked,
+    through the tensor binding and through the C entry point."""
     A, B = inputs.batched_small()
-    out = f.gemm_nt_batched(_dev(A), _dev(B))
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
     ref, bound = oracle.gemm_nt_batched(A, B)
-    ok, worst, n_bad = oracle.within_bound(got, ref, bound)
+    a, b = _dev(A), _dev(B)
+    out = f.gemm_nt_batched(a, b)
+    torch.cuda.synchronize()
+    ok, worst, n_bad = oracle.within_bound(out.cpu().numpy(), ref, bound)
     assert ok, f"{n_bad} bad, worst {worst:.3g}"
+    P, M, K = A.shape
+    N = B.shape[1]
+    raw = torch.full((P, M, N), SENTINEL, dtype=torch.float32, device="cuda")
+    f.gemm_nt_f16f32_batched(a.data_ptr(), b.data_ptr(), raw.data_ptr(), M, N, K, K, K, N, P, M * K, N * K, M * N,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(raw, out), "the C entry point and the tensor binding differ"
 
 
 def test_batched_equals_single_calls(f):
