@@ -190,6 +190,9 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--match", required=True)
     t.add_argument("--algorithmic-bytes", type=float, required=True)
+    t.add_argument("--expected-fetch-bytes", type=float, default=None,
+                   help="the fetch the tiling cannot avoid (reported beside the measured one)")
+    t.add_argument("--expected-note", default="", help="how --expected-fetch-bytes follows from the tiling")
     t.add_argument("--source-hash", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
@@ -268,6 +271,10 @@ def main(argv=None):
             f"l2_miss_bytes_per_launch = {tr['l2_miss_bytes_per_launch']:.0f}",
             f"algorithmic_bytes_per_launch = {a.algorithmic_bytes:.0f}",
             f"traffic_over_algorithmic = {tr['l2_miss_bytes_per_launch'] / a.algorithmic_bytes:.3f}",
+            *([f"# expected fetch: {a.expected_note}",
+               f"expected_fetch_bytes = {a.expected_fetch_bytes:.0f}",
+               f"fetch_over_expected = {tr['fetch_bytes'] / a.expected_fetch_bytes:.4f}"]
+              if a.expected_fetch_bytes else []),
             f"dispatches = {tr['dispatches'][0]} fetch, {tr['dispatches'][1]} write",
             f"source_hash = {a.source_hash}",
         ]) + "\n"

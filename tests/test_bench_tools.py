@@ -123,3 +123,19 @@ def test_counters_derive_clock_and_busy(tmp_path):
     assert derived["clock_ghz_at_trace_duration"] == pytest.approx(cycles / 900e3)
     assert derived["lds_conflict_cycles_per_active_cycle"] == pytest.approx(0.01)
     assert derived["dispatches_used_per_pass"] == 2
+
+
+def test_traffic_summary_reports_the_expected_fetch(tmp_path):
+    gib_kib = (1 << 30) / 1024
+    fetch = _write_csv(tmp_path / "fetch.csv", COUNTER_HEADER, [
+        [1, "gemm<A>", "FETCH_SIZE", 500_000, 0, 1], [2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", gib_kib / 2, 0, 1]])
+    write = _write_csv(tmp_path / "write.csv", COUNTER_HEADER, [
+        [1, "gemm<A>", "WRITE_SIZE", 1000, 0, 1], [2, "__amd_rocclr_copyBuffer", "WRITE_SIZE", gib_kib, 0, 1]])
+    out = tmp_path / "t.txt"
+    bench_profile.main(["traffic", "--fetch", fetch, "--write", write, "--match", "gemm<A>",
+                        "--algorithmic-bytes", "1e9", "--expected-fetch-bytes", str(500_000 * 2048),
+                        "--expected-note", "by hand", "--source-hash", "h", "--command", "c", "--out", str(out)])
+    kv = dict(line.split(" = ", 1) for line in out.read_text().splitlines() if " = " in line and line[0] != "#")
+    assert float(kv["fetch_over_expected"]) == pytest.approx(1.0)
+    assert float(kv["expected_fetch_bytes"]) == 500_000 * 2048
+    assert kv["source_hash"] == "h"
