@@ -185,3 +185,18 @@ def test_matmul_binding_reads_storage_order_from_strides(f):
         assert oracle.within_bound(out.double().cpu().numpy(), ref, bound)[0]
     with pytest.raises(ValueError):
         f.matmul(a_mk[:, ::2], b_kn[:40])           # no unit stride
+
+
+@pytest.mark.parametrize("a_order,b_order", [("k", "k")] + LAYOUTS)
+@pytest.mark.parametrize("M,N", [(4096, 4096), (300, 520)])          # 128x128 and 128x64 tiles
+@pytest.mark.parametrize("ab,out_fmt,acc", [("f16", "f32", False), ("bf16", "bf16", False), ("f16", "f16", True)])
+def test_k_zero(f, a_order, b_order, M, N, ab, out_fmt, acc):
+    """K = 0: no MFMA runs, so the output is the zero sum (fresh) or the previous
+    values (accumulating), exactly, in every storage order; padding untouched."""
+    rng = np.random.default_rng(M + N)
+    A = _draw((M, 0), rng, ab)
+    B = _draw((N, 0), rng, ab)
+    C = _c_values((M, N), out_fmt, seed=M + 2 * N) if acc else None
+    got, pad_same = _run(f, A, B, ab, out_fmt, a_order, b_order, C, ldo_pad=3)
+    assert pad_same, "padding of Out written"
+    assert np.array_equal(got, C if acc else np.zeros((M, N)))
