@@ -326,3 +326,31 @@ def test_small_grid_batched(f):
         ref, bound = oracle.gemm_nt_batched(A, B)
         ok, worst, n_bad = oracle.within_bound(out.cpu().numpy(), ref, bound)
         assert ok, f"{plan} batch: {n_bad} bad, worst {worst:.3g}"
+
+
+def test_two_streams_at_once(f):
+    """The library keeps no device state between calls: products and fragment
+    copies enqueued on two streams (default priority) that run concurrently
+    give the results each gives alone."""
+    rng = np.random.default_rng(61)
+    A1, B1 = inputs.uniform_f16((1000, 600), rng), inputs.uniform_f16((700, 600), rng)
+    A2, B2 = inputs.uniform_f16((2304, 384), rng), inputs.uniform_f16((2048, 384), rng)
+    img = inputs.random_bits_u16(64 * 4 * 4096, rng)
+    a1, b1, a2, b2 = _dev(A1), _dev(B1), _dev(A2), _dev(B2)
+    src = torch.from_numpy(img.view(np.int16)).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs1, outs2, frags = [], [], []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            outs1.append(f.gemm_nt(a1, b1))
+            frags.append(f.frag_copy(src, torch.empty_like(src), 4, False, 0))
+        with torch.cuda.stream(s2):
+            outs2.append(f.gemm_nt(a2, b2))
+    torch.cuda.synchronize()
+    want_frag = oracle.frag_load(img, 4, False)
+    for o1, o2, fr in zip(outs1, outs2, frags):
+        _assert_parity(o1.cpu().numpy(), A1, B1)
+        _assert_parity(o2.cpu().numpy(), A2, B2)
+        assert np.array_equal(fr.cpu().numpy().view(np.uint32), want_frag)
+    assert all(torch.equal(o, outs1[0]) for o in outs1) and all(torch.equal(o, outs2[0]) for o in outs2)
