@@ -354,3 +354,39 @@ def test_two_streams_at_once(f):
         _assert_parity(o2.cpu().numpy(), A2, B2)
         assert np.array_equal(fr.cpu().numpy().view(np.uint32), want_frag)
     assert all(torch.equal(o, outs1[0]) for o in outs1) and all(torch.equal(o, outs2[0]) for o in outs2)
+
+
+def test_hip_graph_replays(f):
+    """The calls enqueue kernels only (no allocation, no host synchronisation), so
+    they can be captured in a HIP graph: each replay, with new operand values
+    written eagerly between replays, matches the oracle."""
+    rng = np.random.default_rng(71)
+    M, N, K = 640, 384, 320
+    a = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    b = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    src = torch.empty(64 * 2 * 1000, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm the binding and library on the side stream
+        f.gemm_nt(a, b, out=out)
+        f.frag_copy(src, dst, 2, True, 0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f.gemm_nt(a, b, out=out)
+        f.frag_copy(src, dst, 2, True, 0)
+    for _ in range(3):
+        A, B = inputs.uniform_f16((M, K), rng), inputs.uniform_f16((N, K), rng)
+        img = inputs.random_bits_u16(src.numel(), rng)
+        a.copy_(torch.from_numpy(A))
+        b.copy_(torch.from_numpy(B))
+        src.copy_(torch.from_numpy(img.view(np.int16)))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_parity(out.cpu().numpy(), A, B)
+        assert np.array_equal(dst.cpu().numpy().view(np.uint32), oracle.frag_load(img, 2, True))
