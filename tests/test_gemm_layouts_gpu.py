@@ -200,3 +200,20 @@ def test_k_zero(f, a_order, b_order, M, N, ab, out_fmt, acc):
     got, pad_same = _run(f, A, B, ab, out_fmt, a_order, b_order, C, ldo_pad=3)
     assert pad_same, "padding of Out written"
     assert np.array_equal(got, C if acc else np.zeros((M, N)))
+
+
+@pytest.mark.parametrize("a_order,b_order,ab,out_fmt", [("mn", "mn", "bf16", "bf16"), ("k", "mn", "f16", "f16")])
+def test_full_size_16bit_outputs_every_element(f, a_order, b_order, ab, out_fmt):
+    """8192^3 with MN-contiguous operands and a 16-bit output (tied accumulators,
+    transposed for the LDS-staged epilogue), every element checked."""
+    n = 8192
+    A, B = inputs.large_square_bf16(n) if ab == "bf16" else inputs.large_square(n)
+    a = torch.from_numpy(np.ascontiguousarray(_bits(A if a_order == "k" else A.T, ab)).view(np.int16)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(_bits(B if b_order == "k" else B.T, ab)).view(np.int16)).cuda()
+    out = torch.full((n, n), float("nan"), dtype=TORCH[out_fmt], device="cuda")
+    assert f.plan_ex(n, n, n, 1, ORDER[a_order], ORDER[b_order]).startswith("wg256")
+    f.gemm_ex_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), n, n, n, n, n, n, 1, 0, 0, 0,
+                  ORDER[a_order], ORDER[b_order], CODE[ab], CODE[out_fmt], False,
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check_all_rows(out, lambda r0, r1: oracle.gemm_nt_ex(A[r0:r1], B, ab=ab), out_fmt)
