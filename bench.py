@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --pmc-pass        # short run for rocprofv3 --pmc counter passes
+    python bench.py --vendor-sweep    # fp16 -> fp16 products against torch.mm, one JSON line
 
 A step is one gemm_nt_f16f32 launch over the 8192^3 synthetic workload
 (A, B ~ normal(0,1) * 0.1 rounded to fp16, seed 4), inputs resident in HBM.
@@ -504,6 +505,46 @@ def run_secondary(torch, f, stream, a, b, A, B):
     return sec
 
 
+SWEEP_SHAPES = [(1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (4096, 4096, 4096),
+                (5120, 5120, 5120), (8192, 8192, 8192), (4096, 4096, 1024), (8192, 8192, 1024),
+                (8192, 8192, 2048), (6144, 6144, 2048), (1536, 1536, 8192), (512, 512, 16384),
+                (1024, 1024, 4096), (768, 768, 2048), (2048, 8192, 8192), (1024, 8192, 8192),
+                (8192, 1024, 8192), (1024, 8192, 1024), (2048, 2048, 8192), (16384, 8, 16384),
+                (16384, 16, 16384)]
+
+
+def vendor_sweep(torch, f, rounds=5):
+    """Context, not part of the headline: fp16 operands -> fp16 output through
+    gemm_nt and through torch.mm (the vendor BLAS; B passed as a contiguous K x N
+    copy of its transpose) on the same data, interleaved, median per shape."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    stream = torch.cuda.current_stream()
+    timer = StreamTimer(torch, stream)
+    out = []
+    for M, N, K in SWEEP_SHAPES:
+        a = (torch.randn((M, K), device="cuda", generator=g) * 0.1).half()
+        b = (torch.randn((N, K), device="cuda", generator=g) * 0.1).half()
+        bt = b.t().contiguous()
+        o_lib = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        o_own = torch.empty((M, N + (-N) % 8), dtype=torch.float16, device="cuda")[:, :N]
+        calls = {"torch_mm": lambda: torch.mm(a, bt, out=o_lib), "gemm_nt": lambda: f.gemm_nt(a, b, out=o_own)}
+        reps = max(5, min(200, int(2e12 / (2.0 * M * N * K))))
+        for fn in calls.values():
+            for _ in range(3):
+                fn()
+        t = {k: [] for k in calls}
+        for _ in range(rounds):
+            for k, fn in calls.items():
+                t[k].append(timer.time(fn, reps) * 1e3)
+        lib_us, own_us = statistics.median(t["torch_mm"]), statistics.median(t["gemm_nt"])
+        out.append({"shape": [M, N, K], "plan": f.plan(M, N, K), "torch_mm_us": round(lib_us, 2),
+                    "gemm_nt_us": round(own_us, 2), "speedup": round(lib_us / own_us, 3),
+                    "outputs_identical": bool(torch.equal(o_lib, o_own))})
+        del a, b, bt, o_lib, o_own
+    return {"kind": "vendor_sweep", "dtype": "fp16 in, fp16 out", "data": "synthetic normal(0,1)*0.1",
+            "rounds": rounds, "results": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,6 +553,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--vendor-sweep", action="store_true", help="gemm_nt against torch.mm over SWEEP_SHAPES")
     ap.add_argument("--headline-first", action="store_true",
                     help="time the headline before the secondary measurements (default: after them)")
     args = ap.parse_args()
@@ -528,6 +570,9 @@ def main():
         raise RuntimeError("bench.py needs a ROCm GPU")
     if args.pmc_pass:
         pmc_pass(torch, f)
+        return
+    if args.vendor_sweep:
+        print(json.dumps(vendor_sweep(torch, f)), flush=True)
         return
 
     M = N = K = 8192
